@@ -1,0 +1,11 @@
+"""CPU float64 oracle for segment attention — test infrastructure, never on the product path.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package. It shares no code with the HIP library.
+"""
+from .attention import (attend, attention, attention_rows, bf16_to_f64, decode_kv,
+                        e4m3fn_to_f64, merge_partials, request_slots, split_merge,
+                        visible_keys)
+
+__all__ = ["attend", "attention", "attention_rows", "bf16_to_f64", "decode_kv", "e4m3fn_to_f64",
+           "merge_partials", "request_slots", "split_merge", "visible_keys"]
