@@ -1,0 +1,256 @@
+"""Segment attention for MI355X (gfx950): Python binding of libsegattn.so.
+
+Thin ctypes marshalling over the C ABI in include/seg_attn.h: torch tensors supply device
+memory and the current stream; every step of the computation runs in the library's HIP
+kernels. If the library has not been built, every call raises.
+
+    out = prefill(q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_q, cu_seqlens_k,
+                  max_seqlen_q, max_seqlen_k, causal=True)
+    out = decode(q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_k, max_seqlen_k,
+                 k_scale=None, v_scale=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["prefill", "decode", "decode_num_splits", "decode_workspace_bytes", "validate_tables",
+           "status_string", "version", "library_path", "SegAttnError", "KV_BF16", "KV_FP8_E4M3"]
+
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+HEAD_DIM = 128
+GROUP = 8
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsegattn.so")
+_lib = None
+
+
+class SegAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m attention_segmented_kv_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.seg_attn_prefill.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, F32, I32, P, P, P]
+    lib.seg_attn_prefill.restype = I32
+    lib.seg_attn_decode.argtypes = [P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, I64, F32, I32,
+                                    P, P, P, SZ, P]
+    lib.seg_attn_decode.restype = I32
+    lib.seg_attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.seg_attn_decode_workspace_bytes.restype = SZ
+    lib.seg_attn_decode_num_splits.argtypes = [I32, I32, I32, I32, I32, ctypes.POINTER(I32)]
+    lib.seg_attn_decode_num_splits.restype = I32
+    lib.seg_attn_status_string.argtypes = [I32]
+    lib.seg_attn_status_string.restype = ctypes.c_char_p
+    lib.seg_attn_validate_tables.argtypes = [P, I64, P, P, P, I32, I64, I32, ctypes.POINTER(I64)]
+    lib.seg_attn_validate_tables.restype = I32
+    lib.seg_attn_version.argtypes = []
+    lib.seg_attn_version.restype = I32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return _load().seg_attn_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(_load().seg_attn_version())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, name: str, dtypes, device: torch.device, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, has shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_tables(segs, seg_indptr, cu, device, batch_plus_1, names):
+    _check(segs, names[0], (torch.int32,), device, 2)
+    if segs.shape[1] != 2:
+        raise ValueError(f"{names[0]} must have shape [nseg, 2]")
+    _check(seg_indptr, names[1], (torch.int32,), device, 1)
+    if seg_indptr.shape[0] != batch_plus_1:
+        raise ValueError(f"{names[1]} must have batch + 1 entries")
+    for t, nm in zip(cu, names[2:]):
+        _check(t, nm, (torch.int32,), device, 1)
+        if t.shape[0] != batch_plus_1:
+            raise ValueError(f"{nm} must have batch + 1 entries")
+
+
+def prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Tensor,
+            seg_indptr: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+            max_seqlen_q: int, max_seqlen_k: int, *, causal: bool = True,
+            softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Varlen (chunked) prefill over a segmented KV pool; see seg_attn_prefill in seg_attn.h.
+
+    q [total_q, Hq, 128] bf16; k_pool/v_pool [pool_tokens, Hkv, 128] bf16; segs [nseg, 2]
+    int32 (pool_offset, length); seg_indptr, cu_seqlens_q, cu_seqlens_k [B+1] int32.
+    Returns out [total_q, Hq, 128] bf16 (and lse [total_q, Hq] fp32 if return_lse)."""
+    lib = _load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    _check(q, "q", (torch.bfloat16,), dev, 3)
+    _check(k_pool, "k_pool", (torch.bfloat16,), dev, 3)
+    _check(v_pool, "v_pool", (torch.bfloat16,), dev, 3)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape")
+    batch = cu_seqlens_q.shape[0] - 1
+    _check_tables(segs, seg_indptr, (cu_seqlens_q, cu_seqlens_k), dev, batch + 1,
+                  ("segs", "seg_indptr", "cu_seqlens_q", "cu_seqlens_k"))
+    total_q, hq, d = q.shape
+    pool_tokens, hkv, dk = k_pool.shape
+    if dk != d:
+        raise ValueError("q and k_pool head dims differ")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", (torch.bfloat16,), dev, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", (torch.float32,), dev, 2)
+        if tuple(lse.shape) != (total_q, hq):
+            raise ValueError("lse must have shape [total_q, Hq]")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.seg_attn_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(segs), _ptr(seg_indptr),
+                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, int(max_seqlen_q),
+                                  int(max_seqlen_k), hq, hkv, d, pool_tokens, float(softmax_scale),
+                                  1 if causal else 0, _ptr(out), _ptr(lse), stream)
+    if st != 0:
+        raise SegAttnError("seg_attn_prefill", st)
+    return (out, lse) if return_lse else out
+
+
+def decode_num_splits(batch: int, max_seqlen_k: int, num_heads_kv: int = 8, kv_dtype: int = KV_BF16,
+                      num_splits: int = 0):
+    """(num_splits, split_len) the decode call will use on the current device."""
+    ln = ctypes.c_int32(0)
+    n = _load().seg_attn_decode_num_splits(batch, max_seqlen_k, num_heads_kv, kv_dtype, num_splits,
+                                           ctypes.byref(ln))
+    if n < 0:
+        raise ValueError("invalid sizes for decode_num_splits")
+    return int(n), int(ln.value)
+
+
+def decode_workspace_bytes(batch: int, max_seqlen_k: int, num_heads_q: int = 64, num_heads_kv: int = 8,
+                           head_dim: int = HEAD_DIM, kv_dtype: int = KV_BF16, num_splits: int = 0) -> int:
+    return int(_load().seg_attn_decode_workspace_bytes(batch, max_seqlen_k, num_heads_q, num_heads_kv,
+                                                      head_dim, kv_dtype, num_splits))
+
+
+def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Tensor,
+           seg_indptr: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, *,
+           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+           softmax_scale: Optional[float] = None, num_splits: int = 0,
+           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Single-token decode with split-K and a log-sum-exp merge; see seg_attn_decode.
+
+    q [B, Hq, 128] bf16; k_pool/v_pool [pool_tokens, Hkv, 128] bf16, or float8_e4m3fn with
+    k_scale/v_scale [pool_tokens, Hkv] fp32. A workspace is allocated here unless given."""
+    lib = _load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    _check(q, "q", (torch.bfloat16,), dev, 3)
+    fp8 = k_pool.dtype == torch.float8_e4m3fn
+    kv_types = (torch.float8_e4m3fn,) if fp8 else (torch.bfloat16,)
+    _check(k_pool, "k_pool", kv_types, dev, 3)
+    _check(v_pool, "v_pool", kv_types, dev, 3)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape")
+    batch, hq, d = q.shape
+    pool_tokens, hkv, _ = k_pool.shape
+    _check_tables(segs, seg_indptr, (cu_seqlens_k,), dev, batch + 1,
+                  ("segs", "seg_indptr", "cu_seqlens_k"))
+    if fp8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("an fp8 pool needs k_scale and v_scale")
+        for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _check(t, nm, (torch.float32,), dev, 2)
+            if tuple(t.shape) != (pool_tokens, hkv):
+                raise ValueError(f"{nm} must have shape [pool_tokens, Hkv]")
+    kv_dtype = KV_FP8_E4M3 if fp8 else KV_BF16
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", (torch.bfloat16,), dev, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if return_lse and lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", (torch.float32,), dev, 2)
+    with torch.cuda.device(dev):
+        need = int(lib.seg_attn_decode_workspace_bytes(batch, int(max_seqlen_k), hq, hkv, d, kv_dtype,
+                                                       int(num_splits)))
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.seg_attn_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                 kv_dtype, _ptr(segs), _ptr(seg_indptr), _ptr(cu_seqlens_k), batch,
+                                 int(max_seqlen_k), hq, hkv, d, pool_tokens, float(softmax_scale),
+                                 int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                 stream)
+    if st != 0:
+        raise SegAttnError("seg_attn_decode", st)
+    return (out, lse) if return_lse else out
+
+
+def validate_tables(segs, seg_indptr, cu_seqlens_k, pool_tokens: int, *, cu_seqlens_q=None,
+                    causal: bool = True):
+    """Host-side table check (seg_attn_validate_tables). Accepts CPU tensors or numpy arrays.
+    Returns (status, bad_index)."""
+    import numpy as np
+    lib = _load()
+    as_np = lambda a: np.ascontiguousarray(
+        (a.detach().cpu().numpy() if isinstance(a, torch.Tensor) else np.asarray(a)).astype(np.int32))
+    s = as_np(segs).reshape(-1, 2)
+    ind = as_np(seg_indptr)
+    ck = as_np(cu_seqlens_k)
+    cq = None if cu_seqlens_q is None else as_np(cu_seqlens_q)
+    bad = ctypes.c_int64(0)
+    st = lib.seg_attn_validate_tables(s.ctypes.data if s.size else None, s.shape[0], ind.ctypes.data,
+                                      None if cq is None else cq.ctypes.data, ck.ctypes.data,
+                                      len(ck) - 1, int(pool_tokens), 1 if causal else 0,
+                                      ctypes.byref(bad))
+    return int(st), int(bad.value)

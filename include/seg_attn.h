@@ -1,0 +1,160 @@
+/*
+ * seg_attn.h — C ABI of the MI355X (gfx950) segment-attention library (libsegattn.so).
+ *
+ * The operation is GQA attention, softmax(scale * Q K^T + mask) V, evaluated with an online
+ * softmax, where each request's keys and values are not a dense tensor but a few contiguous
+ * runs ("segments") of a shared token pool. This is the SegmentAttention kernel of the Flood
+ * inference framework (Flood README, "Introduction": the KV cache is managed as segmentable
+ * blocks instead of paged blocks, which keeps each request's cache contiguous; "Kernels /
+ * Seg-attn": 64 query heads, 8 kv heads, head dim 128, measured against flash-attn's varlen
+ * forward). Two entry points cover the hot path: a varlen prefill (whole or chunked, causal or
+ * not) and a single-token decode that splits each request's keys into blocks, computes partial
+ * results per block and reduces them per request with a log-sum-exp merge (FlashAccel article,
+ * "data layout": blockwise partial attention reduced per request; the running max m_i and
+ * normaliser l_i of "FlashAttention on Ascend NPU", bottleneck 2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers:   every array argument is a DEVICE pointer unless marked HOST. All buffers are
+ *             owned by the caller; the library never allocates, frees or retains them.
+ * Streams:    work is enqueued on `stream` (0 = the null stream) and the call returns without
+ *             waiting. Device-side faults surface at the caller's next synchronisation.
+ * Errors:     every call returns a seg_attn_status_t. Argument errors the host can see are
+ *             reported before anything is launched; nothing is printed and no C++ exception
+ *             crosses the ABI. The device-resident tables (segments, cu_seqlens) are trusted on
+ *             the hot path: check them with seg_attn_validate_tables on host copies if needed.
+ * Layouts:    q / out          [total_q, Hq, D]   bf16, row-major, contiguous
+ *             k_pool / v_pool  [pool_tokens, Hkv, D] bf16 or fp8 (OCP E4M3FN), contiguous:
+ *                              each (token, kv head) row is D contiguous elements
+ *             k_scale/v_scale  [pool_tokens, Hkv]  fp32, FP8 pools only: a stored code c at
+ *                              (token, head) means the value c * scale[token, head]
+ *             lse              [total_q, Hq] fp32, natural log; -inf for a row with no key
+ *             segs             [nseg] seg_attn_segment_t; request b owns
+ *                              segs[seg_indptr[b] .. seg_indptr[b+1]) and its logical keys are
+ *                              those segments concatenated in table order
+ *             cu_seqlens_q/k   [B+1] int32 prefix sums: request b has
+ *                              Lq_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] queries and
+ *                              K_b = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys; K_b must equal
+ *                              the sum of its segments' lengths
+ * Heads:      query head h reads kv head h / (Hq / Hkv) (consecutive query heads share one).
+ * Causal:     aligned bottom-right: query i of request b sits at key position K_b - Lq_b + i
+ *             and sees keys 0 .. K_b - Lq_b + i (this is what chunked prefill needs).
+ * Supported:  head_dim == 128 and Hq / Hkv == 8 (64 q / 8 kv heads, or any Hkv with 8 query
+ *             heads per kv head); other shapes return SEG_ATTN_ERR_UNSUPPORTED.
+ */
+#ifndef SEG_ATTN_H_
+#define SEG_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* seg_attn_stream_t; /* a hipStream_t */
+
+/* One contiguous run of a request's keys: pool slots [pool_offset, pool_offset + length). */
+typedef struct {
+  int32_t pool_offset;
+  int32_t length;
+} seg_attn_segment_t;
+
+typedef int32_t seg_attn_status_t;
+enum {
+  SEG_ATTN_OK = 0,
+  SEG_ATTN_ERR_INVALID_ARG = 1, /* a null pointer, negative size, inconsistent scalar */
+  SEG_ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim != 128 or Hq/Hkv != 8 */
+  SEG_ATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
+  SEG_ATTN_ERR_HIP = 4,         /* the HIP runtime reported an error at launch */
+  SEG_ATTN_ERR_TABLE = 5        /* seg_attn_validate_tables found an inconsistent table */
+};
+
+enum { SEG_ATTN_KV_BF16 = 0, SEG_ATTN_KV_FP8_E4M3 = 1 };
+
+/*
+ * Prefill: attention of a batch of query chunks against their requests' segmented KV.
+ *
+ * q            [total_q, Hq, 128] bf16, total_q = cu_seqlens_q[batch].
+ * k_pool/v_pool[pool_tokens, Hkv, 128] bf16.
+ * segs, seg_indptr, cu_seqlens_q, cu_seqlens_k: as in the header comment (device).
+ * max_seqlen_q, max_seqlen_k: HOST upper bounds of Lq_b and K_b (they size the launch grid;
+ *              rows beyond a request's real length are skipped).
+ * softmax_scale: multiplies Q K^T (1/sqrt(128) for the usual scaling).
+ * causal:      0 or 1. With causal, Lq_b > K_b is invalid (not checked on the device).
+ * out          [total_q, Hq, 128] bf16, written for every query row of every request.
+ * lse          [total_q, Hq] fp32 or NULL.
+ * Returns SEG_ATTN_OK, or an error before anything is launched.
+ */
+seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
+                                   const seg_attn_segment_t* segs, const int32_t* seg_indptr,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                   int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                   int64_t pool_tokens, float softmax_scale, int32_t causal,
+                                   void* out, float* lse, seg_attn_stream_t stream);
+
+/*
+ * Decode: one query token per request (Q_len = 1) against all K_b keys of its segments.
+ *
+ * q            [batch, Hq, 128] bf16.
+ * k_pool/v_pool[pool_tokens, Hkv, 128]: bf16 when kv_dtype == SEG_ATTN_KV_BF16, E4M3FN codes
+ *              (1 byte each) when kv_dtype == SEG_ATTN_KV_FP8_E4M3.
+ * k_scale/v_scale [pool_tokens, Hkv] fp32 for FP8 (required), ignored (may be NULL) for bf16.
+ * cu_seqlens_k [batch+1] int32; max_seqlen_k: HOST upper bound of K_b.
+ * num_splits   number of key blocks per request; 0 picks one from max_seqlen_k, batch and the
+ *              device's compute-unit count. Keys of request b are cut into blocks of
+ *              ceil(max_seqlen_k / num_splits) rounded up to a multiple of 64; each block's
+ *              partial (O_s, LSE_s) goes to the workspace and a second kernel merges them.
+ * out          [batch, Hq, 128] bf16; lse [batch, Hq] fp32 or NULL.
+ * workspace    device scratch of at least seg_attn_decode_workspace_bytes(...) bytes for the
+ *              same (batch, max_seqlen_k, num_heads_q, head_dim, num_splits); may be NULL when
+ *              that size is 0. Its contents need no initialisation and are clobbered.
+ */
+seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                                  const float* k_scale, const float* v_scale, int32_t kv_dtype,
+                                  const seg_attn_segment_t* segs, const int32_t* seg_indptr,
+                                  const int32_t* cu_seqlens_k, int32_t batch,
+                                  int32_t max_seqlen_k, int32_t num_heads_q, int32_t num_heads_kv,
+                                  int32_t head_dim, int64_t pool_tokens, float softmax_scale,
+                                  int32_t num_splits, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, seg_attn_stream_t stream);
+
+/* Bytes of workspace seg_attn_decode needs for these arguments on the current device (0 when
+ * one split suffices). Returns 0 also for invalid sizes; seg_attn_decode reports those. */
+size_t seg_attn_decode_workspace_bytes(int32_t batch, int32_t max_seqlen_k, int32_t num_heads_q,
+                                       int32_t num_heads_kv, int32_t head_dim, int32_t kv_dtype,
+                                       int32_t num_splits);
+
+/* The split count seg_attn_decode uses for these arguments on the current device: the given
+ * num_splits clamped to what max_seqlen_k allows, or the automatic choice for 0. Writes the
+ * keys per split to *split_len when it is not NULL. Returns -1 on invalid sizes. */
+int32_t seg_attn_decode_num_splits(int32_t batch, int32_t max_seqlen_k, int32_t num_heads_kv,
+                                   int32_t kv_dtype, int32_t num_splits, int32_t* split_len);
+
+/* Static text for a status code; never NULL. */
+const char* seg_attn_status_string(seg_attn_status_t status);
+
+/*
+ * Check HOST copies of the tables against each other and the pool: every segment inside
+ * [0, pool_tokens) with length >= 0, seg_indptr and cu_seqlens non-decreasing from 0, each
+ * request's segment lengths summing to K_b, Lq_b <= K_b when causal, no two segments of the
+ * whole table overlapping. cu_seqlens_q may be NULL (decode: Lq_b = 1). On failure returns
+ * SEG_ATTN_ERR_TABLE and, if bad_index is not NULL, stores the offending request (or segment,
+ * for overlaps and out-of-pool segments) index there.
+ */
+seg_attn_status_t seg_attn_validate_tables(const seg_attn_segment_t* segs, int64_t nseg,
+                                           const int32_t* seg_indptr,
+                                           const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_k, int32_t batch,
+                                           int64_t pool_tokens, int32_t causal,
+                                           int64_t* bad_index);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t seg_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEG_ATTN_H_ */

@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the header declares,
+and rejects bad arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seg_attn.h")
+
+sa = pytest.importorskip("attention_segmented_kv_amd")
+
+
+def _lib():
+    if not os.path.exists(sa.library_path()):
+        pytest.skip("libsegattn.so not built")
+    return sa._load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(seg_attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("seg_attn_prefill", "seg_attn_decode", "seg_attn_decode_workspace_bytes",
+              "seg_attn_decode_num_splits", "seg_attn_status_string", "seg_attn_validate_tables",
+              "seg_attn_version"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    raw = ctypes.CDLL(sa.library_path())
+    for s in declared_symbols():
+        assert hasattr(raw, s), f"{s} not exported"
+    assert lib.seg_attn_version() == 10000
+
+
+def test_status_strings():
+    _lib()
+    assert sa.status_string(0) == "ok"
+    for st in range(1, 6):
+        assert sa.status_string(st) not in ("ok", "unknown status")
+    assert sa.status_string(99) == "unknown status"
+
+
+def _prefill_args(**over):
+    a = dict(q=1, k=1, v=1, segs=1, ind=1, cq=1, ck=1, batch=1, mq=4, mk=4, hq=64, hkv=8, d=128,
+             pool=16, scale=0.1, causal=1, out=1, lse=None, stream=None)
+    a.update(over)
+    return [a[k] for k in ("q", "k", "v", "segs", "ind", "cq", "ck", "batch", "mq", "mk", "hq", "hkv",
+                           "d", "pool", "scale", "causal", "out", "lse", "stream")]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(segs=None), 1), (dict(batch=-1), 1),
+    (dict(mq=-3), 1), (dict(d=64), 2), (dict(hq=32), 2), (dict(hq=60), 1), (dict(hkv=0), 1),
+    (dict(causal=2), 1), (dict(mq=8, mk=4), 1), (dict(scale=float("nan")), 1), (dict(pool=-1), 1),
+])
+def test_prefill_rejects_bad_arguments(over, status):
+    lib = _lib()
+    assert lib.seg_attn_prefill(*_prefill_args(**over)) == status
+
+
+def test_prefill_empty_batch_is_a_noop():
+    lib = _lib()
+    assert lib.seg_attn_prefill(*_prefill_args(batch=0, q=None, out=None)) == 0
+
+
+def _decode_args(**over):
+    a = dict(q=1, k=1, v=1, ks=None, vs=None, kvd=0, segs=1, ind=1, ck=1, batch=2, mk=100, hq=64,
+             hkv=8, d=128, pool=16, scale=0.1, ns=1, out=1, lse=None, ws=None, wsb=0, stream=None)
+    a.update(over)
+    return [a[k] for k in ("q", "k", "v", "ks", "vs", "kvd", "segs", "ind", "ck", "batch", "mk", "hq",
+                           "hkv", "d", "pool", "scale", "ns", "out", "lse", "ws", "wsb", "stream")]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(kvd=7), 1), (dict(kvd=1), 1), (dict(kvd=1, ks=1), 1), (dict(d=96), 2),
+    (dict(ns=-1), 1), (dict(mk=-1), 1), (dict(ns=4), 3), (dict(ns=4, ws=1, wsb=16), 3),
+])
+def test_decode_rejects_bad_arguments(over, status):
+    lib = _lib()
+    assert lib.seg_attn_decode(*_decode_args(**over)) == status
+
+
+def test_split_plan_and_workspace_size():
+    _lib()
+    n, ln = sa.decode_num_splits(4, 1000, 8, sa.KV_BF16, 4)
+    assert n == 4 and ln == 256 and ln % 64 == 0 and n * ln >= 1000
+    n, ln = sa.decode_num_splits(4, 1000, 8, sa.KV_BF16, 1)
+    assert n == 1 and ln >= 1000
+    n, ln = sa.decode_num_splits(4, 100, 8, sa.KV_BF16, 1000)  # clamped to 64-key splits
+    assert n == 2 and ln == 64
+    for bsz, mk, kvd in ((128, 8192, 0), (16, 131072, 1), (1, 50, 0), (3, 0, 0)):
+        n, ln = sa.decode_num_splits(bsz, mk, 8, kvd, 0)
+        assert n >= 1 and ln % 64 == 0 and n * ln >= mk and (n - 1) * ln < max(mk, 1)
+        ws = sa.decode_workspace_bytes(bsz, mk, 64, 8, 128, kvd, 0)
+        if n == 1:
+            assert ws == 0
+        else:
+            assert ws >= bsz * 64 * n * (128 + 1) * 4
+    assert sa.decode_workspace_bytes(4, 1000, 64, 8, 64, 0, 4) == 0  # unsupported head dim
+
+
+def test_validate_tables_accepts_good_and_flags_bad():
+    _lib()
+    import workloads as wl
+    w = wl.make_random(3, batch=3, q_lens=[2, 5, 1], k_lens=[9, 20, 4], max_segs=4, num_heads_q=8,
+                       num_heads_kv=1, head_dim=8, zero_length_segments=True)
+    segs, ind, cq, ck = wl.host_tables(w)
+    st, bad = sa.validate_tables(segs, ind, ck, w.pool_tokens, cu_seqlens_q=cq)
+    assert (st, bad) == (0, -1)
+    # a request's lengths no longer add up
+    ck2 = ck.copy(); ck2[2:] += 1
+    assert sa.validate_tables(segs, ind, ck2, w.pool_tokens, cu_seqlens_q=cq)[0] == 5
+    # a segment out of the pool
+    s2 = segs.copy(); s2[0, 0] = w.pool_tokens
+    assert sa.validate_tables(s2, ind, ck, w.pool_tokens, cu_seqlens_q=cq) == (5, 0)
+    # two segments overlapping
+    nz = [i for i in range(len(segs)) if segs[i, 1] > 0]
+    s3 = segs.copy(); s3[nz[1], 0] = s3[nz[0], 0]
+    assert sa.validate_tables(s3, ind, ck, w.pool_tokens, cu_seqlens_q=cq)[0] == 5
+    # causal with more queries than keys
+    cq2 = np.array([0, 2, 7, 12])
+    assert sa.validate_tables(segs, ind, ck, w.pool_tokens, cu_seqlens_q=cq2) == (5, 2)
+    assert sa.validate_tables(segs, ind, ck, w.pool_tokens, cu_seqlens_q=cq2, causal=False)[0] == 0
