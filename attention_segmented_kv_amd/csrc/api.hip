@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -13,7 +14,7 @@ namespace segattn {
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool, const void* segs,
                           const int32_t* seg_indptr, const int32_t* cu_q, const int32_t* cu_k,
                           int batch, int max_seqlen_q, int hkv, float scale, int causal, void* out,
-                          float* lse, hipStream_t stream);
+                          float* lse, int cu_count, int force_tile, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int fp8, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,
@@ -78,6 +79,14 @@ bool plan_splits(int batch, int max_k, int hkv, int fp8, int requested, int* n_o
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// SEG_ATTN_PREFILL_TILE=128 or 256 pins the prefill tiling (tests use it to cover both).
+int prefill_tile_override() {
+  const char* v = std::getenv("SEG_ATTN_PREFILL_TILE");
+  if (v == nullptr) return 0;
+  const int t = std::atoi(v);
+  return (t == 128 || t == 256) ? t : 0;
+}
+
 size_t workspace_for(int batch, int hq, int n_splits) {
   if (n_splits <= 1) return 0;
   const size_t rows = (size_t)batch * hq * n_splits;
@@ -131,7 +140,8 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
     if (grid > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
     hipError_t e = segattn::launch_prefill(q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_q,
                                            cu_seqlens_k, batch, max_seqlen_q, num_heads_kv,
-                                           softmax_scale, causal, out, lse, (hipStream_t)stream);
+                                           softmax_scale, causal, out, lse, current_cu_count(),
+                                           prefill_tile_override(), (hipStream_t)stream);
     return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
   } catch (...) {
     return SEG_ATTN_ERR_HIP;

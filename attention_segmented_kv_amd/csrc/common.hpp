@@ -78,7 +78,10 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, lds_void_t* lds_bas
 __device__ __forceinline__ void copy4_to_lds(const void* g, lds_void_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, lds_base, 4, 0, 0);
 }
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their "no wait" maxima). Issued through the
+// builtin, not inline asm, so the compiler's own wait insertion knows every earlier vector
+// memory operation, HBM->LDS copies included, has completed here.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Transposing LDS read: within each group of 16 lanes, lane i receives element (i % 4) of the
 // 4 bf16 values addressed by lane 4 * jj + i / 4, for jj = 0..3.

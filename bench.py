@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the segment-attention hot path on one MI355X.
+
+Default: the single causal prefill of the Seg-attn kernel table's shape (batch 1,
+Q_len = K_len = 1024, 64 q / 8 kv heads, d = 128, bf16, KV in one segment of a 16384-slot
+pool). One step = one seg_attn_prefill call over that batch; the headline value is
+causal-adjusted TFLOPS (4 * d * Hq * visible (q, k) pairs per second). The other workloads
+(chunked prefill, bf16 decode, FP8 long decode) are measured in the same run and reported
+under "configs" (prefill: TFLOPS; decode: KV-read GB/s), unless --quick.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--quick] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+KERNEL_SOURCES = {"prefill": "attention_segmented_kv_amd/csrc/prefill.hip",
+                  "decode": "attention_segmented_kv_amd/csrc/decode.hip"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(kind: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kind]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def prefill_flops(w) -> float:
+    return 4.0 * w.head_dim * w.num_heads_q * w.visible_pairs()
+
+
+def decode_kv_bytes(w) -> float:
+    per_tok = w.num_heads_kv * w.head_dim * (2 if w.kv_dtype == "bf16" else 1) * 2
+    if w.kv_dtype != "bf16":
+        per_tok += w.num_heads_kv * 4 * 2  # one fp32 scale each for K and V
+    return float(w.k_lens.sum()) * per_tok
+
+
+def make_step(w):
+    import attention_segmented_kv_amd as sa
+    import torch
+    if w.kind == "prefill":
+        out = torch.empty_like(w.q)
+
+        def step():
+            sa.prefill(w.q, w.k_pool, w.v_pool, w.segs, w.seg_indptr, w.cu_seqlens_q, w.cu_seqlens_k,
+                       w.max_seqlen_q, w.max_seqlen_k, causal=w.causal, softmax_scale=w.softmax_scale,
+                       out=out)
+        return step
+    out = torch.empty_like(w.q)
+    kvd = sa.KV_FP8_E4M3 if w.kv_dtype == "fp8_e4m3" else sa.KV_BF16
+    need = sa.decode_workspace_bytes(w.batch, w.max_seqlen_k, w.num_heads_q, w.num_heads_kv, w.head_dim, kvd, 0)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.q.device)
+
+    def step():
+        sa.decode(w.q, w.k_pool, w.v_pool, w.segs, w.seg_indptr, w.cu_seqlens_k, w.max_seqlen_k,
+                  k_scale=w.k_scale, v_scale=w.v_scale, softmax_scale=w.softmax_scale, out=out,
+                  workspace=ws)
+    return step
+
+
+def time_steps(step, steps: int, warmup: int):
+    """W untimed steps, then K timed steps between two device synchronisations. Each call is
+    also bracketed by a pair of events on the stream the kernels run on (torch's current
+    stream, which the binding passes to the library) for the per-launch duration."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = sum(per) / len(per)
+    return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "launch_ms_mean": mean,
+            "launch_ms_median": per[len(per) // 2], "launch_ms_min": per[0]}
+
+
+def load_traffic(kind: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they were taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(kind):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The oracle, as it stands, on the host cores: whole-workload passes of the prefill
+    workload repeated until about budget_s seconds have been spent."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    segs, ind, cq, ck = wl.host_tables(w)
+    qb, kb, vb = wl.bits(w.q), wl.bits(w.k_pool), wl.bits(w.v_pool)
+    passes, t_total = 0, 0.0
+    while t_total < budget_s and passes < 50:
+        t0 = time.perf_counter()
+        oracle.attention(qb, kb, vb, segs, ind, cq, ck, num_heads_kv=w.num_heads_kv,
+                         softmax_scale=w.softmax_scale, causal=w.causal)
+        t_total += time.perf_counter() - t0
+        passes += 1
+    tflops = prefill_flops(w) * passes / t_total / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the whole workload (all 64 heads x {int(w.q_lens.sum())} "
+                      f"query rows), float64 numpy, {t_total:.1f} s total"}
+
+
+def measure(w, steps, warmup, kind):
+    step = make_step(w)
+    t = time_steps(step, steps, warmup)
+    if kind == "prefill":
+        work = prefill_flops(w)
+        achieved = work / (t["launch_ms_mean"] * 1e-3) / 1e12
+        per_step = work / (t["ms_per_step"] * 1e-3) / 1e12
+        rf = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+              "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic("prefill", w.name)}
+        return per_step, "TFLOP/s", rf, t, work
+    work = decode_kv_bytes(w)
+    achieved = work / (t["launch_ms_mean"] * 1e-3) / 1e9
+    per_step = work / (t["ms_per_step"] * 1e-3) / 1e9
+    rf = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+          "frac": achieved / PEAK_HBM_GBS, "traffic": load_traffic("decode", w.name),
+          "note": "per call: split kernel + merge kernel"}
+    return per_step, "GB/s", rf, t, work
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the segment-attention path is built and timed on a single "
+              "MI355X; runs on more than one GPU are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    import attention_segmented_kv_amd as sa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sa._load()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    head_c = args.config
+    log(f"[bench] generating headline workload config {head_c}")
+    w_cpu = wl.make_config(head_c, device="cpu", poison=True) if head_c in (1, 2, 3) else None
+    w = w_cpu.to(dev) if w_cpu is not None else wl.make_config(head_c, device=dev)
+    kind = w.kind
+    log(f"[bench] timing {w.name}: warmup {args.warmup}, steps {args.steps}")
+    value, unit, roof, t, work = measure(w, args.steps, args.warmup, kind)
+    log(f"[bench] {w.name}: {value:.2f} {unit} per step, launch mean {t['launch_ms_mean']*1e3:.1f} us, "
+        f"roofline frac {roof['frac']:.3f}")
+
+    result = {
+        "metric": "causal-adj attention TFLOPS (prefill) + KV-read GB/s (decode), 64q/8kv/d128",
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8_e4m3 kv / bf16 mfma",
+        "data": "synthetic",
+        "config": {"workload": w.name, "recipe": w.recipe, "batch": w.batch,
+                   "q_len": int(w.q_lens.max()), "k_len": int(w.k_lens.max()), "heads_q": w.num_heads_q,
+                   "heads_kv": w.num_heads_kv, "head_dim": w.head_dim, "causal": w.causal,
+                   "seed": w.seed, "parallelism": "single GPU"},
+        "roofline": roof,
+        "timing": {k: round(v, 6) for k, v in t.items()},
+        "work_per_step": work,
+    }
+
+    if not args.quick:
+        extra = []
+        for c in (1, 2, 3, 4, 5):
+            if c == head_c:
+                continue
+            log(f"[bench] config {c}: generating")
+            wc = wl.make_config(c, device=dev)
+            v, u, rf, tc, wk = measure(wc, max(20, args.steps // 2), args.warmup, wc.kind)
+            log(f"[bench] {wc.name}: {v:.2f} {u}, launch mean {tc['launch_ms_mean']*1e3:.1f} us, frac {rf['frac']:.3f}")
+            extra.append({"workload": wc.name, "value": round(v, 3), "unit": u,
+                          "launch_us_mean": round(tc["launch_ms_mean"] * 1e3, 2),
+                          "roofline": rf, "work_per_step": wk})
+            del wc
+            torch.cuda.empty_cache()
+        result["configs"] = extra
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        wb = w_cpu if w_cpu is not None else wl.make_config(2, device="cpu")
+        result["cpu_baseline"] = cpu_baseline(wb)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

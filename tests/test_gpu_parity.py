@@ -17,6 +17,16 @@ pytestmark = pytest.mark.gpu
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
 
 
+@pytest.fixture(params=["auto", "128", "256"])
+def prefill_tile(request, monkeypatch):
+    """Run a prefill test with the library's automatic tiling and with each tiling forced."""
+    if request.param != "auto":
+        monkeypatch.setenv("SEG_ATTN_PREFILL_TILE", request.param)
+    else:
+        monkeypatch.delenv("SEG_ATTN_PREFILL_TILE", raising=False)
+    return request.param
+
+
 def _report(name, mx, rms):
     print(f"[parity] {name}: max_abs={mx:.3e} rms={rms:.3e}", flush=True)
 
@@ -35,21 +45,21 @@ def _full_compare(w, name, num_splits=0):
 # ---------------------------------------------------------------- the named workloads
 
 @needs_gpu
-def test_config1_tiny_prefill_full():
+def test_config1_tiny_prefill_full(prefill_tile):
     print("[case] config 1 tiny prefill", flush=True)
     w = wl.make_config(1).to("cuda")
     _full_compare(w, "config1")
 
 
 @needs_gpu
-def test_config2_prefill_1k_full():
+def test_config2_prefill_1k_full(prefill_tile):
     print("[case] config 2 prefill 1024", flush=True)
     w = wl.make_config(2).to("cuda")
     _full_compare(w, "config2")
 
 
 @needs_gpu
-def test_config3_chunked_prefill_sampled():
+def test_config3_chunked_prefill_sampled(prefill_tile):
     print("[case] config 3 chunked prefill (sampled rows)", flush=True)
     w = wl.make_config(3, device="cuda")
     out, lse = H.run_gpu(w)
@@ -112,7 +122,7 @@ RAGGED_PREFILL = [
 
 @needs_gpu
 @pytest.mark.parametrize("case", RAGGED_PREFILL, ids=[f"seed{c[0]}" for c in RAGGED_PREFILL])
-def test_prefill_ragged_full(case):
+def test_prefill_ragged_full(case, prefill_tile):
     seed, ql, kl, causal, ms = case
     print(f"[case] ragged prefill seed={seed} q={ql} k={kl} causal={causal}", flush=True)
     w = wl.make_random(seed, batch=len(ql), q_lens=ql, k_lens=kl, max_segs=ms, causal=causal,
@@ -121,7 +131,7 @@ def test_prefill_ragged_full(case):
 
 
 @needs_gpu
-def test_prefill_noncausal_empty_keys_gives_zero_and_neg_inf_lse():
+def test_prefill_noncausal_empty_keys_gives_zero_and_neg_inf_lse(prefill_tile):
     print("[case] non-causal prefill with K=0", flush=True)
     w = wl.make_random(18, batch=2, q_lens=[3, 4], k_lens=[0, 7], causal=False).to("cuda")
     out, lse = _full_compare(w, "empty-keys")
@@ -129,7 +139,7 @@ def test_prefill_noncausal_empty_keys_gives_zero_and_neg_inf_lse():
 
 
 @needs_gpu
-def test_prefill_small_heads_multiple_kv_heads():
+def test_prefill_small_heads_multiple_kv_heads(prefill_tile):
     print("[case] prefill Hq=16 Hkv=2", flush=True)
     w = wl.make_random(19, batch=2, q_lens=[40, 9], k_lens=[50, 130], num_heads_q=16,
                        num_heads_kv=2).to("cuda")
@@ -162,7 +172,7 @@ def test_decode_ragged_full(case):
 # ---------------------------------------------------------------- invariants on the device
 
 @needs_gpu
-def test_prefill_is_bitwise_deterministic_and_layout_invariant():
+def test_prefill_is_bitwise_deterministic_and_layout_invariant(prefill_tile):
     print("[case] determinism + re-layout", flush=True)
     w = wl.make_random(31, batch=2, q_lens=[100, 37], k_lens=[250, 37], max_segs=1).to("cuda")
     o1 = H.run_gpu(w, return_lse=False)
@@ -196,7 +206,7 @@ def test_prefill_is_bitwise_deterministic_and_layout_invariant():
 
 
 @needs_gpu
-def test_causal_first_row_returns_first_value_exactly():
+def test_causal_first_row_returns_first_value_exactly(prefill_tile):
     print("[case] first causal row = v0", flush=True)
     w = wl.make_random(32, batch=1, q_lens=[40], k_lens=[40], max_segs=3).to("cuda")
     out = H.run_gpu(w, return_lse=False)
@@ -220,7 +230,7 @@ def test_decode_splits_agree_and_match_prefill_last_row():
 
 
 @needs_gpu
-def test_chunked_prefill_equals_suffix_of_full_prefill():
+def test_chunked_prefill_equals_suffix_of_full_prefill(prefill_tile):
     print("[case] chunked = suffix", flush=True)
     full = wl.make_random(34, batch=1, q_lens=[512], k_lens=[512], max_segs=4).to("cuda")
     o_full = H.run_gpu(full, return_lse=False).float()
