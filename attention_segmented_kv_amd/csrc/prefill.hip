@@ -54,6 +54,7 @@ struct BlockCursor {
   const Segment* segs;
   int idx, end, start, off, len;
   __device__ __forceinline__ void fetch() {
+    idx = __builtin_amdgcn_readfirstlane(idx);  // uniform index -> scalar (s_load) table read
     if (idx < end) {
       i32x2 v = *reinterpret_cast<const i32x2*>(segs + idx);
       off = __builtin_amdgcn_readfirstlane(v[0]);
@@ -276,11 +277,13 @@ __global__ __launch_bounds__(kThreads) void prefill_split_kernel(
     if (ip < 0 || ip >= n_pairs || blk >= n_blocks) return;
     const int kb0 = blk * kBlockN;
     if (kb0 + kBlockN > kfull) {
+      const int thr = row_limit - kb0 - 4 * h;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int j = kb0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (j >= row_limit) s0[e] = -INFINITY;
-        if (j + 32 >= row_limit) s1[e] = -INFINITY;
+        // key kb0 + 4h + off_e is hidden iff off_e >= thr (off_e a compile-time constant)
+        const int off_e = 8 * (e >> 2) + (e & 3);
+        if (off_e >= thr) s0[e] = -INFINITY;
+        if (off_e + 32 >= thr) s1[e] = -INFINITY;
       }
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), s0[2]);
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void prefill_split_kernel(
 // copied into LDS serves 256 rows, half the L2->LDS traffic of the 128-row tiles) and run in
 // opposite phases: in step j group 0 issues its MFMAs (PV of block j-1, S of block j) while
 // group 1 runs the softmax of block j-1, then the roles swap. K and V blocks are double
-// buffered and copied one step ahead of use.
+// buffered and copied one step ahead of use; the Q tile is staged in LDS.
 constexpr int kWidePos = 32;
 
 template <bool kCausal>
@@ -436,6 +439,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
   __shared__ __attribute__((aligned(1024))) char kr1[kBlkBytes];
   __shared__ __attribute__((aligned(1024))) char vr0[kBlkBytes];
   __shared__ __attribute__((aligned(1024))) char vr1[kBlkBytes];
+  __shared__ __attribute__((aligned(1024))) char qlds[2 * kWidePos * kGroup * kHeadDim];  // 256 rows
 
   // Work item: kv head fastest (with 8 kv heads, head g always runs on XCD g), then the query
   // tiles of one request, heaviest (last) first, then the requests. Workgroups running at the
@@ -471,13 +475,23 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
   const int kfull = kCausal ? min(K, K - lq + wpos0 + 1) : K;  // every row of this wave sees these
   const int row_limit = kCausal ? min(K, K - lq + pos + 1) : K;
 
-  bf16x8 qf[8];
+  // Q tile staged in LDS (kept out of registers): LDS row R = wave * 32 + n holds the query row
+  // of wave R / 32, lane row n; chunk c of row R sits at chunk position c ^ (R % 16). Thread t
+  // copies chunk position t % 16 of rows t / 16 + 32 i; rows past the request re-read its last
+  // query row (they are computed but never stored).
   {
-    const bf16_t* qrow = q + ((int64_t)(q0 + pos) * hq + head) * kHeadDim + 8 * h;
 #pragma unroll
-    for (int step = 0; step < 8; ++step)
-      qf[step] = row_valid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * step) : bf16x8{};
+    for (int i = 0; i < 8; ++i) {
+      const int R = (tid >> 4) + 32 * i;
+      const int rw = R >> 5, rn = R & 31;
+      const int rpos = min(p0 + 16 * (rw >> 2) + 4 * (rw & 3) + (rn >> 3), lq - 1);
+      const int rhead = g * kGroup + (rn & 7);
+      const int c = (tid & 15) ^ (R & 15);
+      const bf16_t* src = q + ((int64_t)(q0 + rpos) * hq + rhead) * kHeadDim + c * 8;
+      copy16_to_lds(src, (lds_void_t*)((lds_char_t*)qlds + i * 8192 + wave * 1024));
+    }
   }
+  const lds_char_t* qmine = (const lds_char_t*)qlds + (wave * 32 + n) * 256;
 
   BlockCursor kcur, vcur;
   kcur.init(segs, seg_indptr[b], seg_indptr[b + 1]);
@@ -505,40 +519,41 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     a.base = (int64_t)cur.off + (kb0 - cur.start);
     a.s0 = a.s1 = 0;
     if (!a.fast) {
+      // Walk the segments the block overlaps with a scalar copy of the cursor: every lane
+      // takes the same trip and the table is read with scalar loads, so no vector memory
+      // wait (which would also wait for the prefetched K/V) is needed.
       const int r0 = min(kb0 + crow, last), r1 = min(kb0 + 32 + crow, last);
-      SegCursor c2;
-      c2.segs = cur.segs;
-      c2.idx = cur.idx;
-      c2.end = cur.end;
-      c2.start = cur.start;
-      c2.off = cur.off;
-      c2.len = cur.len;
-      a.s0 = c2.slot(r0);
-      a.s1 = c2.slot(r1);
+      BlockCursor c2 = cur;
+      while (true) {
+        if (r0 - c2.start >= 0 && r0 - c2.start < c2.len) a.s0 = (int64_t)c2.off + (r0 - c2.start);
+        if (r1 - c2.start >= 0 && r1 - c2.start < c2.len) a.s1 = (int64_t)c2.off + (r1 - c2.start);
+        if (last - c2.start < c2.len) break;
+        c2.start += c2.len;
+        ++c2.idx;
+        c2.fetch();
+      }
     }
     return a;
   };
-  auto copy_k = [&](const BlockAddr& a, char* dst) __attribute__((always_inline)) {
-    lds_char_t* lk = (lds_char_t*)dst + wave * 1024;
-    if (a.fast) {
-      const char* sb = (const char*)(kbase + a.base * tok_stride);
-      copy16_to_lds(sb + koff0, (lds_void_t*)lk);
-      copy16_to_lds(sb + koff1, (lds_void_t*)(lk + 8192));
-    } else {
-      copy16_to_lds(kbase + a.s0 * tok_stride + kchunk * 8, (lds_void_t*)lk);
-      copy16_to_lds(kbase + a.s1 * tok_stride + kchunk * 8, (lds_void_t*)(lk + 8192));
-    }
+  // K/V blocks travel HBM -> registers -> LDS. Loading into registers two steps ahead of the
+  // LDS write hides the HBM latency of blocks no workgroup has touched yet, and plain register
+  // loads let the compiler wait for exactly the data it needs.
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  auto load_rows = [&](BlockCursor& cur, int blk, const bf16_t* pool_base, int chunk, uint32_t off0,
+                       uint32_t off1, u32x4& r0, u32x4& r1) __attribute__((always_inline)) {
+    const BlockAddr a = block_addr(cur, blk);
+    // one load per row on every path (no branch around the loads), from either address form
+    const char* sb = (const char*)(pool_base + a.base * tok_stride);
+    const char* p0 = a.fast ? sb + off0 : (const char*)(pool_base + a.s0 * tok_stride + chunk * 8);
+    const char* p1 = a.fast ? sb + off1 : (const char*)(pool_base + a.s1 * tok_stride + chunk * 8);
+    r0 = *(const u32x4*)p0;
+    r1 = *(const u32x4*)p1;
   };
-  auto copy_v = [&](const BlockAddr& a, char* dst) __attribute__((always_inline)) {
-    lds_char_t* lv = (lds_char_t*)dst + wave * 1024;
-    if (a.fast) {
-      const char* sb = (const char*)(vbase + a.base * tok_stride);
-      copy16_to_lds(sb + voff0, (lds_void_t*)lv);
-      copy16_to_lds(sb + voff1, (lds_void_t*)(lv + 8192));
-    } else {
-      copy16_to_lds(vbase + a.s0 * tok_stride + vchunk * 8, (lds_void_t*)lv);
-      copy16_to_lds(vbase + a.s1 * tok_stride + vchunk * 8, (lds_void_t*)(lv + 8192));
-    }
+  // Thread tid's two 16-byte pieces of a block go to bytes tid*16 and 8192 + tid*16 of its slot
+  // (the swizzle is in which global chunk the thread loaded).
+  auto store_rows = [&](char* dst, const u32x4& r0, const u32x4& r1) __attribute__((always_inline)) {
+    *(__attribute__((address_space(3))) u32x4*)((lds_char_t*)dst + tid * 16) = r0;
+    *(__attribute__((address_space(3))) u32x4*)((lds_char_t*)dst + 8192 + tid * 16) = r1;
   };
 
   f32x16 o[4];
@@ -585,8 +600,9 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
         const int r0 = n, r1 = 32 + n;
         bf16x8 a0 = lds_read16(kb + r0 * 256 + ((c ^ (r0 & 15)) << 4));
         bf16x8 a1 = lds_read16(kb + r1 * 256 + ((c ^ (r1 & 15)) << 4));
-        s0 = mfma32x32x16(a0, qf[step], s0);
-        s1 = mfma32x32x16(a1, qf[step], s1);
+        const bf16x8 qv = lds_read16(qmine + ((c ^ (n & 15)) << 4));
+        s0 = mfma32x32x16(a0, qv, s0);
+        s1 = mfma32x32x16(a1, qv, s1);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -596,11 +612,13 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     if (j < 0 || j >= n_blocks) return;
     const int kb0 = j * kBlockN;
     if (kb0 + kBlockN > kfull) {
+      const int thr = row_limit - kb0 - 4 * h;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int jj = kb0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (jj >= row_limit) s0[e] = -INFINITY;
-        if (jj + 32 >= row_limit) s1[e] = -INFINITY;
+        // key kb0 + 4h + off_e is hidden iff off_e >= thr (off_e a compile-time constant)
+        const int off_e = 8 * (e >> 2) + (e & 3);
+        if (off_e >= thr) s0[e] = -INFINITY;
+        if (off_e + 32 >= thr) s1[e] = -INFINITY;
       }
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(s0[0], s0[1]), s0[2]);
@@ -634,44 +652,57 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     pb[3] = to_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
   };
 
-  // Step j: read K(j) from slot j % 2 and V(j-1) from slot (j-1) % 2; copy K(j+1) into slot
-  // (j+1) % 2 and V(j) into slot j % 2, to be read from step j+1 on. R = j % 2 as a
-  // compile-time constant.
+  // Register staging sets: set e holds K(j+1) and V(j) at the start of step j with j % 2 == e.
+  u32x4 stk[2][2], stv[2][2];
+  const int last_blk = n_blocks - 1;
+
+  // Step j: K(j) in LDS slot j % 2 is read (S of block j), V(j-1) in slot (j-1) % 2 is read
+  // (PV of block j-1). At the start, staging set j % 2 (loaded two steps earlier) is written to
+  // LDS: K(j+1) into slot (j+1) % 2 and V(j) into slot j % 2, both last read in step j-1; then
+  // the same set is refilled with K(j+3) and V(j+2). Blocks past the end re-load the last one.
   auto step = [&](int j, auto r_c) __attribute__((always_inline)) {
     constexpr int R = decltype(r_c)::value;
     char* kread = R == 0 ? kr0 : kr1;
-    char* kfill = R == 0 ? kr1 : kr0;
+    char* kwrite = R == 0 ? kr1 : kr0;
     char* vread = R == 0 ? vr1 : vr0;
-    char* vfill = R == 0 ? vr0 : vr1;
-    const bool fill_k = j + 1 < n_blocks;
-    const bool fill_v = j < n_blocks;
-    BlockAddr ka{}, va{};
-    if (fill_k) ka = block_addr(kcur, j + 1);
-    if (fill_v) va = block_addr(vcur, j);
-    if (fill_k) copy_k(ka, kfill);
-    if (fill_v) copy_v(va, vfill);
+    char* vwrite = R == 0 ? vr0 : vr1;
+    store_rows(kwrite, stk[R][0], stk[R][1]);
+    store_rows(vwrite, stv[R][0], stv[R][1]);
+    load_rows(kcur, min(j + 3, last_blk), kbase, kchunk, koff0, koff1, stk[R][0], stk[R][1]);
+    load_rows(vcur, min(j + 2, last_blk), vbase, vchunk, voff0, voff1, stv[R][0], stv[R][1]);
     if (grp == 0) gemm_phase(j, vread, kread);
     else softmax_phase(j - 1);
     phase_barrier();
     if (grp == 1) gemm_phase(j, vread, kread);
     else softmax_phase(j);
-    wait_vmem();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS stores are done
     phase_barrier();
   };
 
-  // Prologue: K(0).
-  {
-    BlockAddr a0{};
-    if (n_blocks > 0) a0 = block_addr(kcur, 0);
-    if (n_blocks > 0) copy_k(a0, kr0);
+  // Prologue: K(0) into slot 0; staging set 0 = {K(1), V(0)}, set 1 = {K(2), V(1)}.
+  if (n_blocks > 0) {
+    u32x4 a0, a1;
+    // issue order = use order (set 0 before set 1), so each wait covers only what it needs
+    load_rows(kcur, 0, kbase, kchunk, koff0, koff1, a0, a1);
+    load_rows(kcur, min(1, last_blk), kbase, kchunk, koff0, koff1, stk[0][0], stk[0][1]);
+    load_rows(vcur, 0, vbase, vchunk, voff0, voff1, stv[0][0], stv[0][1]);
+    load_rows(kcur, min(2, last_blk), kbase, kchunk, koff0, koff1, stk[1][0], stk[1][1]);
+    load_rows(vcur, min(1, last_blk), vbase, vchunk, voff0, voff1, stv[1][0], stv[1][1]);
+    store_rows(kr0, a0, a1);
   }
-  wait_vmem();
+  wait_vmem();  // also the Q tile's HBM->LDS copies
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   phase_barrier();
   if (n_blocks > 0) {
-    for (int j = 0; j <= n_blocks; j += 2) {
+    // Both steps of a pair unconditionally inside the loop, the odd tail after it: a loop body
+    // that may end after its first step would make the compiler assume that step's loads are
+    // the most recent ones at the loop head and wait for all of them.
+    int j = 0;
+    for (; j + 1 <= n_blocks; j += 2) {
       step(j, std::integral_constant<int, 0>{});
-      if (j + 1 <= n_blocks) step(j + 1, std::integral_constant<int, 1>{});
+      step(j + 1, std::integral_constant<int, 1>{});
     }
+    if (j <= n_blocks) step(j, std::integral_constant<int, 0>{});
   }
 
   const float l_tot = sum_xor32(l_run);

@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of 1 GiB, 5 times (reference kernel "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the segment-attention path is built and timed on a single "
@@ -178,6 +181,15 @@ def main():
         sys.exit(1)
     sa._load()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 5}}))
+        return
 
     head_c = args.config
     log(f"[bench] generating headline workload config {head_c}")
