@@ -108,7 +108,8 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
  *              partial (O_s, LSE_s) goes to the workspace and a second kernel merges them.
  * out          [batch, Hq, 128] bf16; lse [batch, Hq] fp32 or NULL.
  * workspace    device scratch of at least seg_attn_decode_workspace_bytes(...) bytes for the
- *              same (batch, max_seqlen_k, num_heads_q, head_dim, num_splits); may be NULL when
+ *              same (batch, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, kv_dtype,
+ *              num_splits); may be NULL when
  *              that size is 0. Its contents need no initialisation and are clobbered.
  */
 seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void* v_pool,
