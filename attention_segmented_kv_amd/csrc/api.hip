@@ -18,7 +18,8 @@ hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int fp8, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,
-                         int split_len, int num_splits, float scale, void* out, float* lse,
+                         int forced_len, int min_len, int max_chunks, int cu_count, float scale,
+                         void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* tab,
                          float* ws_o, float* ws_lse, hipStream_t stream);
 }  // namespace segattn
 
@@ -27,8 +28,7 @@ namespace {
 constexpr int kHeadDim = 128;
 constexpr int kGroup = 8;
 constexpr int kMaxDevices = 64;
-constexpr int kSplitGranule = 64;   // split lengths are multiples of this many keys
-constexpr int kMaxAutoSplits = 128;
+constexpr int kChunkGranule = 64;  // decode chunk lengths are multiples of this many keys
 
 int g_cu_count[kMaxDevices];
 std::once_flag g_cu_once[kMaxDevices];
@@ -47,33 +47,31 @@ int current_cu_count() {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Split plan for decode. A split is the key range one workgroup reduces to one partial result.
-// Automatic choice: at least kMinSplit keys per split so each of the workgroup's 4 waves streams
-// several tiles, and no more splits than needed to give every compute unit a few workgroups'
-// worth of units; split lengths are multiples of 64 keys.
-bool plan_splits(int batch, int max_k, int hkv, int fp8, int requested, int* n_out, int* len_out) {
-  if (batch < 0 || max_k < 0 || hkv <= 0 || requested < 0) return false;
-  if (max_k == 0 || batch == 0) {
-    *n_out = 1;
-    *len_out = kSplitGranule;
-    return true;
-  }
-  int64_t n;
+// Decode chunk plan. Each request's keys are cut into chunks of one length; a chunk times a kv
+// head is one work unit of the split pass. With num_splits > 0 the length is fixed here:
+// ceil(max_k / num_splits) rounded up to a multiple of 64, so no request has more than
+// num_splits chunks. With 0 the device picks the length from the total key count (so that every
+// compute unit gets about a dozen units), never below kMinChunk keys, which bounds the chunks per
+// request by ceil(max_k / kMinChunk).
+struct DecodePlan {
+  int forced_len;        // 0: chosen on the device
+  int min_len;           // lower bound of the length
+  int64_t per_request;   // upper bound of the chunks of one request
+};
+
+bool plan_decode(int batch, int max_k, int fp8, int requested, DecodePlan* p) {
+  if (batch < 0 || max_k < 0 || requested < 0) return false;
+  const int min_chunk = fp8 ? 1024 : 512;
   if (requested > 0) {
-    n = requested;
+    const int64_t len = std::max<int64_t>(kChunkGranule, ceil_div(ceil_div(max_k, requested), kChunkGranule) * kChunkGranule);
+    p->forced_len = (int)len;
+    p->min_len = (int)len;
+    p->per_request = std::max<int64_t>(1, ceil_div(max_k, len));
   } else {
-    const int64_t min_split = fp8 ? 1024 : 512;
-    const int64_t units_per_level = (int64_t)batch * hkv;
-    const int64_t want_units = 4LL * current_cu_count();
-    int64_t by_work = ceil_div(want_units, units_per_level);         // splits to fill the chip
-    int64_t by_len = ceil_div(max_k, min_split);                      // splits allowed by length
-    n = std::max<int64_t>(1, std::min(by_len, std::max<int64_t>(by_work, ceil_div(max_k, 4096))));
-    n = std::min<int64_t>(n, kMaxAutoSplits);
+    p->forced_len = 0;
+    p->min_len = min_chunk;
+    p->per_request = std::max<int64_t>(1, ceil_div(max_k, min_chunk));
   }
-  int64_t len = ceil_div(ceil_div(max_k, n), kSplitGranule) * kSplitGranule;
-  n = ceil_div(max_k, len);
-  *n_out = (int)n;
-  *len_out = (int)len;
   return true;
 }
 
@@ -87,10 +85,20 @@ int prefill_tile_override() {
   return (t == 128 || t == 256) ? t : 0;
 }
 
-size_t workspace_for(int batch, int hq, int n_splits) {
-  if (n_splits <= 1) return 0;
-  const size_t rows = (size_t)batch * hq * n_splits;
-  return align_up(rows * kHeadDim * sizeof(float), 256) + align_up(rows * sizeof(float), 256);
+// Decode workspace: [0, 256) plan header, then chunk offsets [batch + 1] int32, the chunk table
+// [max_chunks] x (request, index) int32, the partial LSEs [max_chunks][Hq] fp32 and the partial
+// outputs [max_chunks][Hq][128] fp32, each part 256-byte aligned.
+struct DecodeWs {
+  size_t base, tab, lse, o, total;
+};
+DecodeWs decode_ws_layout(int64_t batch, int64_t hq, int64_t max_chunks) {
+  DecodeWs w;
+  w.base = 256;
+  w.tab = w.base + align_up((size_t)(batch + 1) * 4, 256);
+  w.lse = w.tab + align_up((size_t)max_chunks * 8, 256);
+  w.o = w.lse + align_up((size_t)(max_chunks * hq) * 4, 256);
+  w.total = w.o + (size_t)(max_chunks * hq) * kHeadDim * 4;
+  return w;
 }
 
 seg_attn_status_t check_heads(int32_t hq, int32_t hkv, int32_t head_dim) {
@@ -152,11 +160,12 @@ int32_t seg_attn_decode_num_splits(int32_t batch, int32_t max_seqlen_k, int32_t 
                                    int32_t kv_dtype, int32_t num_splits, int32_t* split_len) {
   try {
     if (kv_dtype != SEG_ATTN_KV_BF16 && kv_dtype != SEG_ATTN_KV_FP8_E4M3) return -1;
-    int n = 0, len = 0;
-    if (!plan_splits(batch, max_seqlen_k, num_heads_kv, kv_dtype == SEG_ATTN_KV_FP8_E4M3, num_splits, &n, &len))
-      return -1;
-    if (split_len) *split_len = len;
-    return n;
+    if (num_heads_kv <= 0) return -1;
+    DecodePlan p;
+    if (!plan_decode(batch, max_seqlen_k, kv_dtype == SEG_ATTN_KV_FP8_E4M3, num_splits, &p)) return -1;
+    if (p.per_request > INT32_MAX) return -1;
+    if (split_len) *split_len = p.min_len;
+    return (int32_t)p.per_request;
   } catch (...) {
     return -1;
   }
@@ -167,9 +176,10 @@ size_t seg_attn_decode_workspace_bytes(int32_t batch, int32_t max_seqlen_k, int3
                                        int32_t num_splits) {
   try {
     if (check_heads(num_heads_q, num_heads_kv, head_dim) != SEG_ATTN_OK) return 0;
-    const int32_t n = seg_attn_decode_num_splits(batch, max_seqlen_k, num_heads_kv, kv_dtype, num_splits, nullptr);
-    if (n < 0) return 0;
-    return workspace_for(batch, num_heads_q, n);
+    if (kv_dtype != SEG_ATTN_KV_BF16 && kv_dtype != SEG_ATTN_KV_FP8_E4M3) return 0;
+    DecodePlan p;
+    if (!plan_decode(batch, max_seqlen_k, kv_dtype == SEG_ATTN_KV_FP8_E4M3, num_splits, &p)) return 0;
+    return decode_ws_layout(batch, num_heads_q, p.per_request * batch).total;
   } catch (...) {
     return 0;
   }
@@ -194,21 +204,18 @@ seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void*
     const bool fp8 = kv_dtype == SEG_ATTN_KV_FP8_E4M3;
     if (!q || !k_pool || !v_pool || !segs || !seg_indptr || !cu_seqlens_k || !out) return SEG_ATTN_ERR_INVALID_ARG;
     if (fp8 && (!k_scale || !v_scale)) return SEG_ATTN_ERR_INVALID_ARG;
-    int n = 0, len = 0;
-    if (!plan_splits(batch, max_seqlen_k, num_heads_kv, fp8, num_splits, &n, &len)) return SEG_ATTN_ERR_INVALID_ARG;
-    const size_t need = workspace_for(batch, num_heads_q, n);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SEG_ATTN_ERR_WORKSPACE;
-    if ((int64_t)n * num_heads_kv * batch > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
-    float* ws_o = nullptr;
-    float* ws_lse = nullptr;
-    if (n > 1) {
-      const size_t rows = (size_t)batch * num_heads_q * n;
-      ws_o = (float*)workspace;
-      ws_lse = (float*)((char*)workspace + align_up(rows * kHeadDim * sizeof(float), 256));
-    }
-    hipError_t e = segattn::launch_decode(q, k_pool, v_pool, k_scale, v_scale, fp8 ? 1 : 0, segs,
-                                          seg_indptr, cu_seqlens_k, batch, num_heads_kv, len, n,
-                                          softmax_scale, out, lse, ws_o, ws_lse, (hipStream_t)stream);
+    DecodePlan p;
+    if (!plan_decode(batch, max_seqlen_k, fp8, num_splits, &p)) return SEG_ATTN_ERR_INVALID_ARG;
+    const int64_t max_chunks = p.per_request * batch;
+    if (max_chunks * num_heads_kv > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
+    const DecodeWs lay = decode_ws_layout(batch, num_heads_q, max_chunks);
+    if (workspace == nullptr || workspace_bytes < lay.total) return SEG_ATTN_ERR_WORKSPACE;
+    char* ws = (char*)workspace;
+    hipError_t e = segattn::launch_decode(
+        q, k_pool, v_pool, k_scale, v_scale, fp8 ? 1 : 0, segs, seg_indptr, cu_seqlens_k, batch,
+        num_heads_kv, p.forced_len, p.min_len, (int)max_chunks, current_cu_count(), softmax_scale, out,
+        lse, (int32_t*)ws, (int32_t*)(ws + lay.base), (int32_t*)(ws + lay.tab), (float*)(ws + lay.o),
+        (float*)(ws + lay.lse), (hipStream_t)stream);
     return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
   } catch (...) {
     return SEG_ATTN_ERR_HIP;

@@ -102,15 +102,18 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
  *              (1 byte each) when kv_dtype == SEG_ATTN_KV_FP8_E4M3.
  * k_scale/v_scale [pool_tokens, Hkv] fp32 for FP8 (required), ignored (may be NULL) for bf16.
  * cu_seqlens_k [batch+1] int32; max_seqlen_k: HOST upper bound of K_b.
- * num_splits   number of key blocks per request; 0 picks one from max_seqlen_k, batch and the
- *              device's compute-unit count. Keys of request b are cut into blocks of
- *              ceil(max_seqlen_k / num_splits) rounded up to a multiple of 64; each block's
- *              partial (O_s, LSE_s) goes to the workspace and a second kernel merges them.
- * out          [batch, Hq, 128] bf16; lse [batch, Hq] fp32 or NULL.
+ * num_splits   0: each request's keys are cut into chunks whose length the device picks from the
+ *              total key count (at least 512 keys for bf16, 1024 for fp8) so that every compute
+ *              unit gets several (chunk, kv head) work units. n > 0: chunks of
+ *              ceil(max_seqlen_k / n) keys rounded up to a multiple of 64, so at most n per
+ *              request. A request cut into one chunk is written directly; otherwise each chunk's
+ *              partial (O_s, LSE_s) goes to the workspace and a merge kernel combines them.
+ * out          [batch, Hq, 128] bf16; lse [batch, Hq] fp32 or NULL. A request with K_b = 0
+ *              gets out = 0 and lse = -inf.
  * workspace    device scratch of at least seg_attn_decode_workspace_bytes(...) bytes for the
  *              same (batch, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, kv_dtype,
- *              num_splits); may be NULL when
- *              that size is 0. Its contents need no initialisation and are clobbered.
+ *              num_splits); always required. It holds the chunk plan and the partial results;
+ *              its contents need no initialisation and are clobbered.
  */
 seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                                   const float* k_scale, const float* v_scale, int32_t kv_dtype,
@@ -121,15 +124,17 @@ seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void*
                                   int32_t num_splits, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, seg_attn_stream_t stream);
 
-/* Bytes of workspace seg_attn_decode needs for these arguments on the current device (0 when
- * one split suffices). Returns 0 also for invalid sizes; seg_attn_decode reports those. */
+/* Bytes of workspace seg_attn_decode needs for these arguments: a 256-byte plan header, the
+ * per-request chunk offsets, the chunk table and one fp32 (O, LSE) partial per chunk and query
+ * head, for the largest chunk count the arguments allow. Returns 0 for invalid or unsupported
+ * sizes; seg_attn_decode reports those. */
 size_t seg_attn_decode_workspace_bytes(int32_t batch, int32_t max_seqlen_k, int32_t num_heads_q,
                                        int32_t num_heads_kv, int32_t head_dim, int32_t kv_dtype,
                                        int32_t num_splits);
 
-/* The split count seg_attn_decode uses for these arguments on the current device: the given
- * num_splits clamped to what max_seqlen_k allows, or the automatic choice for 0. Writes the
- * keys per split to *split_len when it is not NULL. Returns -1 on invalid sizes. */
+/* The largest number of chunks seg_attn_decode cuts one request into for these arguments (at
+ * least 1). Writes the chunk length to *split_len when it is not NULL: the fixed length for
+ * num_splits > 0, the smallest length the device may pick for 0. Returns -1 on invalid sizes. */
 int32_t seg_attn_decode_num_splits(int32_t batch, int32_t max_seqlen_k, int32_t num_heads_kv,
                                    int32_t kv_dtype, int32_t num_splits, int32_t* split_len);
 
