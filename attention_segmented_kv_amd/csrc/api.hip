@@ -19,7 +19,7 @@ hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int fp8, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,
                          int forced_len, int min_len, int max_chunks, int cu_count, float scale,
-                         void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* tab,
+                         void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* recs,
                          float* ws_o, float* ws_lse, hipStream_t stream);
 }  // namespace segattn
 
@@ -85,8 +85,8 @@ int prefill_tile_override() {
   return (t == 128 || t == 256) ? t : 0;
 }
 
-// Decode workspace: [0, 256) plan header, then chunk offsets [batch + 1] int32, the chunk table
-// [max_chunks] x (request, index) int32, the partial LSEs [max_chunks][Hq] fp32 and the partial
+// Decode workspace: [0, 256) plan header, then chunk offsets [batch + 1] int32, the chunk
+// records [max_chunks] x 16 int32, the partial LSEs [max_chunks][Hq] fp32 and the partial
 // outputs [max_chunks][Hq][128] fp32, each part 256-byte aligned.
 struct DecodeWs {
   size_t base, tab, lse, o, total;
@@ -95,7 +95,7 @@ DecodeWs decode_ws_layout(int64_t batch, int64_t hq, int64_t max_chunks) {
   DecodeWs w;
   w.base = 256;
   w.tab = w.base + align_up((size_t)(batch + 1) * 4, 256);
-  w.lse = w.tab + align_up((size_t)max_chunks * 8, 256);
+  w.lse = w.tab + align_up((size_t)max_chunks * 64, 256);
   w.o = w.lse + align_up((size_t)(max_chunks * hq) * 4, 256);
   w.total = w.o + (size_t)(max_chunks * hq) * kHeadDim * 4;
   return w;

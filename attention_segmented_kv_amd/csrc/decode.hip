@@ -139,6 +139,44 @@ __device__ __forceinline__ void v_transposed(const lds_char_t* vb, int kk, bf16x
   }
 }
 
+// A operands of O^T += V^T P^T for the 32 keys 32*kk .. 32*kk + 31 of an fp8 V tile in LDS
+// (128 B rows, 16-byte chunk c of row r at c ^ (r % 8)), still as E4M3FN codes: lane
+// (grp, col) gets the 8 codes V[key(j)][16*dt + col], key(j) as for the bf16 tile. The
+// transposing 8-bit read hands lane i of a 16-lane group byte i % 8 of the 8 bytes addressed by
+// lane 2*j + i / 8, so source lane s of group grp addresses row key(s / 2) at columns
+// 16*dt + 8*(s % 2) .. +7. Issued and waited for in one asm block, as in v_transposed.
+__device__ __forceinline__ void v_transposed8(const lds_char_t* vb, int kk, uint32_t (&lo)[8], uint32_t (&hi)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int s = lane & 15, grp = lane >> 4;
+  const int j = s >> 1;
+  const int key = 32 * kk + 4 * grp + (j < 4 ? j : 12 + j);
+  const int half = 8 * (s & 1);
+  uint32_t pa[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) pa[dt] = (uint32_t)(uintptr_t)(vb + key * 128 + ((dt ^ (key & 7)) << 4) + half);
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 r[8];
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %8\n\t"
+      "ds_read_b64_tr_b8 %1, %9\n\t"
+      "ds_read_b64_tr_b8 %2, %10\n\t"
+      "ds_read_b64_tr_b8 %3, %11\n\t"
+      "ds_read_b64_tr_b8 %4, %12\n\t"
+      "ds_read_b64_tr_b8 %5, %13\n\t"
+      "ds_read_b64_tr_b8 %6, %14\n\t"
+      "ds_read_b64_tr_b8 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7])
+      : "v"(pa[0]), "v"(pa[1]), "v"(pa[2]), "v"(pa[3]), "v"(pa[4]), "v"(pa[5]), "v"(pa[6]), "v"(pa[7])
+      : "memory");
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    lo[dt] = r[dt][0];
+    hi[dt] = r[dt][1];
+  }
+}
+
 // Forward walk over one request's segments with every value wave-uniform, so table reads are
 // scalar loads: they never join the vector-memory queue that the tile copies use.
 struct ScalarCursor {
@@ -162,6 +200,15 @@ struct ScalarCursor {
     start = 0;
     fetch();
   }
+  // Positioned on segment i (whose first key is logical key st) from a chunk record.
+  __device__ __forceinline__ void init_at(const Segment* s, int i, int last, int st, int o, int l) {
+    segs = s;
+    idx = i;
+    end = last;
+    start = st;
+    off = o;
+    len = l;
+  }
   __device__ __forceinline__ void advance_to(int j) {
     while (j - start >= len) {
       start += len;
@@ -171,62 +218,226 @@ struct ScalarCursor {
   }
 };
 
-// Where a unit's keys are: chunk c of request b holds keys [kbeg, kstop).
+// Where a unit's keys are: chunk c of request b holds keys [kbeg, kstop); the segment holding
+// key kbeg is sidx (its first key is logical key sstart, pool slots [soff, soff + slen)).
 struct UnitInfo {
-  int valid, c, g, b, kbeg, kstop, n_tiles;
+  int valid, c, g, b, kbeg, kstop, single, sidx, send, sstart, soff, slen, n_tiles;
 };
 
-// ------------------------------------------------------------------------------------------
-// Plan: chunk length, per-request chunk offsets and the chunk -> (request, index) table.
-// hdr[0] = len, hdr[1] = number of chunks listed (at most max_chunks).
+// One record per chunk, 16 int32 (64 B, one scalar load), stored in schedule order:
+//   0 request b, 1 first key, 2 end key, 3 1 if the chunk is the request's only one,
+//   4 index of the segment holding the first key (segment end index if none), 5 segment end
+//   index of the request, 6 logical first key of that segment, 7 its pool offset, 8 its
+//   length, 9 chunk index (the row of its partial result).
+constexpr int kRecInts = 16;
+constexpr int kBuckets = 256;
+
+// Plan: chunk length, per-request chunk offsets and the chunk records in schedule order. The
+// schedule lists every full-length chunk first, then the shorter last chunks of the requests by
+// decreasing length (a counting sort over 256 length buckets); the split pass deals this list
+// to its columns in snake order, which spreads the short chunks evenly. One thread per request;
+// the table reads are issued together (key counts, segment ranges, then the first segments) so
+// the plan costs few memory latencies.
+// hdr[0] = len, hdr[1] = number of chunks listed (0 if they would not fit in max_chunks).
+constexpr int kPlanSegs = 8;  // segments per request read up front
+
+// Inclusive scan over the 1024 threads of the block of two counts at once: shuffles within each
+// wave, then one pass over the 16 wave totals. wtot is LDS scratch of 2 x 16 ints.
+__device__ __forceinline__ void block_scan2(int& a, int& b, int* wtot) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int ta = __shfl_up(a, d), tb = __shfl_up(b, d);
+    if (lane >= d) {
+      a += ta;
+      b += tb;
+    }
+  }
+  if (lane == 63) {
+    wtot[w] = a;
+    wtot[16 + w] = b;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int x = lane < 16 ? wtot[lane] : 0, y = lane < 16 ? wtot[16 + lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int tx = __shfl_up(x, d), ty = __shfl_up(y, d);
+      if (lane >= d) {
+        x += tx;
+        y += ty;
+      }
+    }
+    if (lane < 16) {
+      wtot[lane] = x;
+      wtot[16 + lane] = y;
+    }
+  }
+  __syncthreads();
+  if (w > 0) {
+    a += wtot[w - 1];
+    b += wtot[16 + w - 1];
+  }
+}
+
+// Plan: chunk length, per-request chunk offsets and the chunk records in schedule order. The
+// schedule lists every full-length chunk first, then the shorter last chunks of the requests by
+// decreasing length (a counting sort over 256 length buckets); the split pass deals this list
+// to its columns in snake order, which spreads the short chunks evenly. One thread per request;
+// the table reads are issued together (key counts, segment ranges, then the first segments) so
+// the plan costs few memory latencies.
+// hdr[0] = len, hdr[1] = number of chunks listed (0 if they would not fit in max_chunks).
 __global__ __launch_bounds__(1024) void decode_plan_kernel(
-    const int32_t* __restrict__ cu_k, int batch, int hkv, int forced_len, int min_len,
+    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ seg_indptr,
+    const Segment* __restrict__ segs, int batch, int hkv, int forced_len, int min_len,
     int target_units, int max_chunks, int32_t* __restrict__ hdr, int32_t* __restrict__ chunk_base,
-    int32_t* __restrict__ tab) {
-  __shared__ int scan[1024];
-  __shared__ int carry_s;
+    int32_t* __restrict__ recs) {
+  __shared__ int wtot[32];
+  __shared__ int hist[kBuckets], bucket_base[kBuckets], bucket_fill[kBuckets];
+  __shared__ int carry_n, carry_f;
   const int tid = threadIdx.x;
+  // This thread's request in the first block, read once and kept for both passes. Every load
+  // is unconditional, at an index clamped into its table, so that they are all in flight at
+  // once (batch >= 1 here).
+  const int bq = min(tid, batch - 1);
+  const int64_t total = (int64_t)cu_k[batch] - cu_k[0];
+  const int nseg = seg_indptr[batch];
+  const int ka = cu_k[bq], kb = cu_k[bq + 1];
+  const int s0 = tid < batch ? seg_indptr[bq] : 0;
+  const int s1 = tid < batch ? seg_indptr[bq + 1] : 0;
+  const int K0 = tid < batch ? kb - ka : 0;
+  Segment sg0[kPlanSegs];
+  if (nseg > 0) {
+#pragma unroll
+    for (int j = 0; j < kPlanSegs; ++j) sg0[j] = segs[min(s0 + j, nseg - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < kPlanSegs; ++j)
+    if (nseg == 0 || s0 + j >= s1) sg0[j] = Segment{0, 0x7fffffff};
   int len = forced_len;
   if (len <= 0) {
-    const int64_t total = (int64_t)cu_k[batch] - cu_k[0];
     int64_t want = (total * hkv + target_units - 1) / target_units;
     want = (want + 63) / 64 * 64;
     len = (int)(want < min_len ? min_len : (want > (1 << 30) ? (1 << 30) : want));
   }
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int b0 = 0; b0 < batch; b0 += 1024) {
-    const int b = b0 + tid;
-    int n = 0;
-    if (b < batch) {
-      const int K = cu_k[b + 1] - cu_k[b];
-      n = K > 0 ? (K + len - 1) / len : 0;
-    }
-    scan[tid] = n;
-    __syncthreads();
-    for (int s = 1; s < 1024; s <<= 1) {  // inclusive Hillis-Steele scan
-      const int add = tid >= s ? scan[tid - s] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
-    }
-    const int carry = carry_s;
-    const int first = carry + scan[tid] - n;
-    if (b < batch) {
-      chunk_base[b] = first;
-      for (int k = 0; k < n && first + k < max_chunks; ++k) {
-        tab[2 * (first + k)] = b;
-        tab[2 * (first + k) + 1] = k;
-      }
-    }
-    __syncthreads();
-    if (tid == 1023) carry_s = carry + scan[1023];
-    __syncthreads();
+  auto counts = [&](int K, int& n, int& f) {
+    n = K > 0 ? (K + len - 1) / len : 0;
+    f = K > 0 ? K / len : 0;
+  };
+  if (tid < kBuckets) {
+    hist[tid] = 0;
+    bucket_fill[tid] = 0;
   }
   if (tid == 0) {
-    chunk_base[batch] = carry_s;
+    carry_n = 0;
+    carry_f = 0;
+  }
+  __syncthreads();
+  // pass 1: totals and the histogram of the short last chunks
+  int n0, f0, sn0 = 0, sf0 = 0;  // counts and inclusive scans of the first block, for pass 2
+  counts(K0, n0, f0);
+  for (int b0 = 0; b0 < batch; b0 += 1024) {
+    const int b = b0 + tid;
+    const int K = b0 == 0 ? K0 : (b < batch ? cu_k[b + 1] - cu_k[b] : 0);
+    int n, f;
+    counts(K, n, f);
+    if (n > f) atomicAdd(&hist[(int)((int64_t)(K - f * len) * kBuckets / len)], 1);
+    int sn = n, sf = f;
+    block_scan2(sn, sf, wtot);
+    if (b0 == 0) {
+      sn0 = sn;
+      sf0 = sf;
+    }
+    if (tid == 1023) {
+      carry_n += sn;
+      carry_f += sf;
+    }
+    __syncthreads();
+  }
+  const int total_n = carry_n, total_f = carry_f;
+  // bucket positions, longest short chunks first: a scan over the buckets in reverse order
+  {
+    int hcount = tid < kBuckets ? hist[kBuckets - 1 - tid] : 0, dummy = 0;
+    block_scan2(hcount, dummy, wtot);
+    if (tid < kBuckets) bucket_base[kBuckets - 1 - tid] = total_f + hcount - hist[kBuckets - 1 - tid];
+  }
+  __syncthreads();
+  // pass 2: chunk offsets and records
+  int cn = 0, cf = 0;  // chunks and full chunks of the blocks before
+  for (int b0 = 0; b0 < batch; b0 += 1024) {
+    const int b = b0 + tid;
+    int K = 0, sa = 0, se = 0, n, f, sn, sf;
+    if (b0 == 0) {
+      K = K0;
+      sa = s0;
+      se = s1;
+      n = n0;
+      f = f0;
+      sn = sn0;
+      sf = sf0;
+    } else {
+      if (b < batch) {
+        K = cu_k[b + 1] - cu_k[b];
+        sa = seg_indptr[b];
+        se = seg_indptr[b + 1];
+      }
+      counts(K, n, f);
+      sn = n;
+      sf = f;
+      block_scan2(sn, sf, wtot);
+    }
+    const int first = cn + sn - n;   // first chunk index of request b
+    const int ffirst = cf + sf - f;  // schedule position of its first full chunk
+    if (b < batch) {
+      chunk_base[b] = first;
+      // walk the request's segments once, in key order, recording where each chunk starts
+      int idx = sa, start = 0;
+      Segment sg = (b0 == 0) ? sg0[0] : (sa < se ? segs[sa] : Segment{0, 0x7fffffff});
+      for (int k = 0; k < n; ++k) {
+        const int kbeg = k * len;
+        while (idx < se && kbeg - start >= sg.length) {
+          start += sg.length;
+          ++idx;
+          const int j = idx - sa;
+          if (b0 == 0 && j < kPlanSegs) {
+            Segment t = sg0[0];
+#pragma unroll
+            for (int q = 1; q < kPlanSegs; ++q) t = (j == q) ? sg0[q] : t;
+            sg = t;
+          } else {
+            sg = idx < se ? segs[idx] : Segment{0, 0x7fffffff};
+          }
+        }
+        int pos = ffirst + k;
+        if (k >= f) {
+          const int bk = (int)((int64_t)(K - f * len) * kBuckets / len);
+          pos = bucket_base[bk] + atomicAdd(&bucket_fill[bk], 1);
+        }
+        if (pos < max_chunks && first + k < max_chunks) {
+          i32x4* r = reinterpret_cast<i32x4*>(recs + (int64_t)pos * kRecInts);
+          r[0] = i32x4{b, kbeg, min(K, kbeg + len), n == 1 ? 1 : 0};
+          r[1] = i32x4{idx, se, start, sg.pool_offset};
+          r[2] = i32x4{sg.length, first + k, 0, 0};
+        }
+      }
+    }
+    // totals of this block for the next one (the last thread holds the block's inclusive sums)
+    if (b0 + 1024 < batch) {
+      __syncthreads();
+      if (tid == 1023) {
+        carry_n = cn + sn;
+        carry_f = cf + sf;
+      }
+      __syncthreads();
+      cn = carry_n;
+      cf = carry_f;
+    }
+  }
+  if (tid == 0) {
+    chunk_base[batch] = total_n;
     hdr[0] = len;
-    hdr[1] = carry_s < max_chunks ? carry_s : max_chunks;
+    // more chunks than the workspace holds means some K_b exceeded max_seqlen_k: list none
+    hdr[1] = total_n <= max_chunks ? total_n : 0;
   }
 }
 
@@ -236,10 +447,8 @@ template <int kFp8>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const bf16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-    const Segment* __restrict__ segs, const int32_t* __restrict__ seg_indptr,
-    const int32_t* __restrict__ cu_k, const int32_t* __restrict__ hdr,
-    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ tab, int hkv,
-    int xcd_spread, float scale, float scale_log2, float* __restrict__ ws_o,
+    const Segment* __restrict__ segs, const int32_t* __restrict__ hdr,
+    const int32_t* __restrict__ recs, int hkv, float scale, float scale_log2, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, bf16_t* __restrict__ out, float* __restrict__ lse) {
   using C = DecodeCfg<kFp8>;
   using L = DecodeLayout<kFp8>;
@@ -250,20 +459,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   __shared__ __attribute__((aligned(1024))) char st1[kWaves * L::kStageBytes];
   __shared__ __attribute__((aligned(16))) float comb[kWaves * L::kCombFloats];
   __shared__ __attribute__((aligned(16))) char qbuf[kQBufs * kQBytes];
+  __shared__ __attribute__((aligned(16))) i32x4 uring[4];
 
-  const int len = rfl(hdr[0]);
-  const int n_units = rfl(hdr[1]) * hkv;
-  const int grid = gridDim.x;
-  // Unit order u = c * hkv + g, dealt round robin. With 8 kv heads and a grid that is a
-  // multiple of 64, the slot permutation puts the 8 heads of a chunk on workgroups of the same
-  // XCD (workgroups go to XCD id % 8), where they share the chunk's scale lines in L2.
-  int slot = blockIdx.x;
-  if (xcd_spread) {
-    const int per = grid >> 3;
-    slot = rfl((blockIdx.x % per) * 8 + blockIdx.x / per);
-  }
-  if (slot >= n_units) return;
-  const int my_units = rfl((n_units - slot + grid - 1) / grid);
+  const int n_chunks = rfl(hdr[1]);
+  // Workgroup = (column p, lane g of the kv heads). Column p takes schedule positions r * P + p
+  // for even r and r * P + P - 1 - p for odd r; in round r its workgroups take kv heads
+  // (g + r) % hkv, so the 8 heads of each chunk are all done and every workgroup meets every
+  // head: the reading speed of a head's slices of the pool rows varies, and this keeps the
+  // workgroups even.
+  const int P = gridDim.x / hkv;
+  const int p = rfl(blockIdx.x / hkv);
+  const int g = rfl(blockIdx.x - p * hkv);
+  const int full_rounds = n_chunks / P;
+  const int last_pos = (full_rounds & 1) ? P - 1 - p : p;
+  const int my_units = full_rounds + (last_pos < n_chunks - full_rounds * P ? 1 : 0);
+  if (my_units == 0) return;
 
   const int tid = threadIdx.x;
   const int wave = rfl(tid >> 6);
@@ -273,22 +483,37 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int hq = hkv * kGroup;
   const int64_t tok_bytes = (int64_t)hkv * C::kRowBytes;
 
-  // Every field is wave-uniform and kept in scalar registers (readfirstlane after each integer
-  // division, which the compiler does on the vector ALU).
+  // Every field is wave-uniform and kept in scalar registers (readfirstlane after the integer
+  // division, which the compiler does on the vector ALU); the chunk record is one scalar load.
   auto unit_info = [&](int r) __attribute__((always_inline)) {
     UnitInfo u;
-    const int id = slot + r * grid;
     u.valid = r < my_units;
-    u.c = u.valid ? rfl(id / hkv) : 0;
-    u.g = rfl(id - u.c * hkv);
-    const i32x2 t = *reinterpret_cast<const i32x2*>(tab + 2 * u.c);
-    u.b = rfl(t[0]);
-    const int k = rfl(t[1]);
-    const int K = rfl(cu_k[u.b + 1] - cu_k[u.b]);
-    u.kbeg = rfl(k * len);
-    u.kstop = rfl(min(K, u.kbeg + len));
+    const int pos = u.valid ? r * P + ((r & 1) ? P - 1 - p : p) : 0;
+    const i32x4* rp = reinterpret_cast<const i32x4*>(recs + (int64_t)pos * kRecInts);
+    const i32x4 r0 = rp[0], r1 = rp[1], r2 = rp[2];
+    u.g = (g + r) % hkv;
+    u.b = rfl(r0[0]);
+    u.kbeg = rfl(r0[1]);
+    u.kstop = rfl(r0[2]);
+    u.single = rfl(r0[3]);
+    u.sidx = rfl(r1[0]);
+    u.send = rfl(r1[1]);
+    u.sstart = rfl(r1[2]);
+    u.soff = rfl(r1[3]);
+    u.slen = rfl(r2[0]);
+    u.c = rfl(r2[1]);
     u.n_tiles = u.valid ? rfl((u.kstop - u.kbeg + C::kTile - 1) / C::kTile) : 0;
     return u;
+  };
+  // Unit identities for the combine, written by wave 0 when it enters a unit (it has a tile in
+  // every unit) and read by all waves between the combine's barriers. Entry r % 4 is rewritten
+  // only once wave 0 works on unit r + 2, after every wave has left the combine of unit r.
+  auto ring_put = [&](const UnitInfo& u, int r) __attribute__((always_inline)) {
+    if (wave == 0 && lane == 0) {
+      i32x4 v = i32x4{u.c, u.g, u.b, u.single};
+      const uint32_t a = (uint32_t)(uintptr_t)((lds_char_t*)uring + 16 * (r & 3));
+      asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+    }
   };
 
   // ---- issue side: this wave's next tile
@@ -296,7 +521,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   int it = wave;  // tile index inside unit iu
   int ir = 0;     // ordinal of unit iu among this workgroup's units
   ScalarCursor cur;
-  cur.init(segs, seg_indptr[iu.b], seg_indptr[iu.b + 1]);
+  cur.init_at(segs, iu.sidx, iu.send, iu.sstart, iu.soff, iu.slen);
+  ring_put(iu, 0);
   auto q_copy = [&](const UnitInfo& u, int r) __attribute__((always_inline)) {
     // wave 0 copies the unit's 8 query rows (2 KiB, contiguous) into Q buffer r % 3
     const char* src = (const char*)(q + ((int64_t)u.b * hq + u.g * kGroup) * kHeadDim) + lane * 16;
@@ -311,7 +537,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       ++ir;
       iu = unit_info(ir);
       if (!iu.valid) return;
-      cur.init(segs, seg_indptr[iu.b], seg_indptr[iu.b + 1]);
+      cur.init_at(segs, iu.sidx, iu.send, iu.sstart, iu.soff, iu.slen);
+      ring_put(iu, ir);
       if (wave == 0) q_copy(iu, ir);
       it = wave;
       if (it < iu.n_tiles) return;
@@ -440,8 +667,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
   // Combine the 4 waves' states for unit r and write the output or the partial.
   auto flush = [&](int r) __attribute__((always_inline)) {
-    const UnitInfo u = unit_info(r);
-    const int nb = rfl(chunk_base[u.b + 1] - chunk_base[u.b]);
     const float l_col = sum_xor32(sum_xor16(l_run));
     float* red = comb + wave * L::kCombFloats;
     if (col < kGroup) {
@@ -461,6 +686,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     }
     wait_lds();
     wg_barrier();
+    i32x4 id4;
+    {
+      const uint32_t a = (uint32_t)(uintptr_t)((lds_char_t*)uring + 16 * (r & 3));
+      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(id4) : "v"(a) : "memory");
+    }
+    const int uc = rfl(id4[0]), ug = rfl(id4[1]), ub = rfl(id4[2]), usingle = rfl(id4[3]);
     const int hh = tid >> 5;        // head 0..7
     const int d4 = (tid & 31) * 4;  // 4 consecutive d
     float mw[kWaves], lw[kWaves];
@@ -486,14 +717,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
     acc *= inv;
     const float lse_v = Lsum > 0.f ? M * scale + __logf(Lsum) : -INFINITY;
-    const int head = u.g * kGroup + hh;
-    if (nb == 1) {
+    const int head = ug * kGroup + hh;
+    if (usingle) {
       bf16x4 v4;
       v4[0] = (bf16_t)acc[0]; v4[1] = (bf16_t)acc[1]; v4[2] = (bf16_t)acc[2]; v4[3] = (bf16_t)acc[3];
-      *reinterpret_cast<bf16x4*>(out + ((int64_t)u.b * hq + head) * kHeadDim + d4) = v4;
-      if (lse != nullptr && (tid & 31) == 0) lse[(int64_t)u.b * hq + head] = lse_v;
+      *reinterpret_cast<bf16x4*>(out + ((int64_t)ub * hq + head) * kHeadDim + d4) = v4;
+      if (lse != nullptr && (tid & 31) == 0) lse[(int64_t)ub * hq + head] = lse_v;
     } else {
-      const int64_t row = (int64_t)u.c * hq + head;
+      const int64_t row = (int64_t)uc * hq + head;
       *reinterpret_cast<f32x4*>(ws_o + row * kHeadDim + d4) = acc;
       if ((tid & 31) == 0) ws_lse[row] = lse_v;
     }
@@ -587,7 +818,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
     for (int kk = 0; kk < kMt / 2; ++kk) {
       bf16x8 vt[8];
+      uint32_t v8lo[8], v8hi[8];
       if constexpr (kFp8 == 0) v_transposed(vb, kk, vt);
+      else v_transposed8(vb, kk, v8lo, v8hi);
       bf16x8 pb = to_bf16x8(s[2 * kk][0], s[2 * kk][1], s[2 * kk][2], s[2 * kk][3], s[2 * kk + 1][0],
                             s[2 * kk + 1][1], s[2 * kk + 1][2], s[2 * kk + 1][3]);
 #pragma unroll
@@ -596,22 +829,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         if constexpr (kFp8 == 0) {
           a = vt[dt];
         } else {
-          // lane needs V[key][d] for d = 16*dt + col and keys 32kk + 4grp + (0..3), +16
-          const int d = 16 * dt + col;
-          const int c = d >> 4;
-          uint32_t w[2];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int r = 32 * kk + 16 * half + 4 * grp + jj;
-              const uint8_t byte = *((const __attribute__((address_space(3))) uint8_t*)(vb + r * 128 + ((c ^ (r & 7)) << 4) + (d & 15)));
-              acc |= (uint32_t)byte << (8 * jj);
-            }
-            w[half] = acc;
-          }
-          a = fp8x8_to_bf16x8(w[0], w[1]);
+          a = fp8x8_to_bf16x8(v8lo[dt], v8hi[dt]);
         }
         o[dt] = mfma16x16x32(a, pb, o[dt]);
       }
@@ -669,7 +887,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
 // One workgroup per (request, kv head): 256 threads = 8 heads x 32 threads x 4 d. Requests
 // listed as one chunk were written by the split pass; requests without keys get O = 0 and
-// LSE = -inf.
+// LSE = -inf. The 32 threads of a head first find the largest partial LSE together, then each
+// accumulates its 4 columns over the chunks four at a time, so the loads overlap.
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws_o,
                                                     const float* __restrict__ ws_lse,
                                                     const int32_t* __restrict__ hdr,
@@ -688,15 +907,32 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
   if (c1 - c0 == 1) return;
   const int64_t row = (int64_t)b * hq + head;
   float M = -INFINITY;
-  for (int c = c0; c < c1; ++c) M = fmaxf(M, ws_lse[(int64_t)c * hq + head]);
+  for (int c = c0 + (tid & 31); c < c1; c += 32) M = fmaxf(M, ws_lse[(int64_t)c * hq + head]);
+#pragma unroll
+  for (int sh = 1; sh < 32; sh <<= 1) M = fmaxf(M, __shfl_xor(M, sh, 32));
   f32x4 acc = f32x4{};
   float Lsum = 0.f;
   if (M != -INFINITY) {
-    for (int c = c0; c < c1; ++c) {
+    int c = c0;
+    for (; c + 4 <= c1; c += 4) {
+      float l[4];
+      f32x4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        l[i] = ws_lse[(int64_t)(c + i) * hq + head];
+        v[i] = *(const f32x4*)(ws_o + ((int64_t)(c + i) * hq + head) * kHeadDim + d4);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float w = __expf(l[i] - M);
+        Lsum += w;
+        acc += w * v[i];
+      }
+    }
+    for (; c < c1; ++c) {
       const float w = __expf(ws_lse[(int64_t)c * hq + head] - M);
       Lsum += w;
-      f32x4 v = *(const f32x4*)(ws_o + ((int64_t)c * hq + head) * kHeadDim + d4);
-      acc += w * v;
+      acc += w * *(const f32x4*)(ws_o + ((int64_t)c * hq + head) * kHeadDim + d4);
     }
   }
   const float inv = Lsum > 0.f ? 1.0f / Lsum : 0.f;
@@ -709,36 +945,36 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
 
 }  // namespace
 
-// Units per workgroup the automatic chunk length aims at.
-constexpr int kUnitsPerWorkgroup = 12;
+// Units per workgroup the automatic chunk length aims at: one per kv head, so that with the
+// per-round head rotation every workgroup meets each head about once.
+constexpr int kUnitsPerWorkgroup = 8;
 
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int fp8, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,
                          int forced_len, int min_len, int max_chunks, int cu_count, float scale,
-                         void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* tab,
+                         void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* recs,
                          float* ws_o, float* ws_lse, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
-  const int64_t max_units = (int64_t)max_chunks * hkv;
-  const int grid = (int)std::min<int64_t>(cu_count, max_units);
+  // columns: one workgroup per (column, kv head), about one workgroup per compute unit
+  const int cols = (int)std::max<int64_t>(1, std::min<int64_t>(cu_count / hkv, max_chunks));
+  const int grid = max_chunks > 0 ? cols * hkv : 0;
   const int target = std::max(1, kUnitsPerWorkgroup * std::max(grid, 1));
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, cu_k, batch, hkv, forced_len,
-                     min_len, target, max_chunks, hdr, chunk_base, tab);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, cu_k, seg_indptr,
+                     (const Segment*)segs, batch, hkv, forced_len, min_len, target, max_chunks, hdr,
+                     chunk_base, recs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (grid > 0) {
     const float scale_log2 = scale * 1.4426950408889634f;
-    const int xcd_spread = (hkv == kGroup && grid % 64 == 0) ? 1 : 0;
     if (fp8) {
       hipLaunchKernelGGL(decode_split_kernel<1>, dim3(grid), dim3(kDecThreads), 0, stream,
-                         (const bf16_t*)q, k_pool, v_pool, k_scale, v_scale, (const Segment*)segs,
-                         seg_indptr, cu_k, hdr, chunk_base, tab, hkv, xcd_spread, scale, scale_log2,
-                         ws_o, ws_lse, (bf16_t*)out, lse);
+                         (const bf16_t*)q, k_pool, v_pool, k_scale, v_scale, (const Segment*)segs, hdr,
+                         recs, hkv, scale, scale_log2, ws_o, ws_lse, (bf16_t*)out, lse);
     } else {
       hipLaunchKernelGGL(decode_split_kernel<0>, dim3(grid), dim3(kDecThreads), 0, stream,
-                         (const bf16_t*)q, k_pool, v_pool, k_scale, v_scale, (const Segment*)segs,
-                         seg_indptr, cu_k, hdr, chunk_base, tab, hkv, xcd_spread, scale, scale_log2,
-                         ws_o, ws_lse, (bf16_t*)out, lse);
+                         (const bf16_t*)q, k_pool, v_pool, k_scale, v_scale, (const Segment*)segs, hdr,
+                         recs, hkv, scale, scale_log2, ws_o, ws_lse, (bf16_t*)out, lse);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

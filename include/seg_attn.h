@@ -125,7 +125,7 @@ seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void*
                                   size_t workspace_bytes, seg_attn_stream_t stream);
 
 /* Bytes of workspace seg_attn_decode needs for these arguments: a 256-byte plan header, the
- * per-request chunk offsets, the chunk table and one fp32 (O, LSE) partial per chunk and query
+ * per-request chunk offsets, a 64-byte record per chunk and one fp32 (O, LSE) partial per chunk and query
  * head, for the largest chunk count the arguments allow. Returns 0 for invalid or unsupported
  * sizes; seg_attn_decode reports those. */
 size_t seg_attn_decode_workspace_bytes(int32_t batch, int32_t max_seqlen_k, int32_t num_heads_q,

@@ -102,8 +102,8 @@ def test_split_plan_and_workspace_size():
         n, ln = sa.decode_num_splits(bsz, mk, 8, kvd, 0)
         assert n >= 1 and ln % 64 == 0 and n * ln >= mk and (n - 1) * ln < max(mk, 1)
         ws = sa.decode_workspace_bytes(bsz, mk, 64, 8, 128, kvd, 0)
-        # plan header + chunk offsets + chunk table + one (O, LSE) partial per chunk and head
-        assert ws >= 256 + (bsz + 1) * 4 + bsz * n * 8 + bsz * 64 * n * (128 + 1) * 4
+        # plan header + chunk offsets + chunk records + one (O, LSE) partial per chunk and head
+        assert ws >= 256 + (bsz + 1) * 4 + bsz * n * 64 + bsz * 64 * n * (128 + 1) * 4
     assert sa.decode_workspace_bytes(4, 1000, 64, 8, 64, 0, 4) == 0  # unsupported head dim
 
 
