@@ -73,27 +73,42 @@ def make_step(w):
     return step
 
 
-def time_steps(step, steps: int, warmup: int):
-    """W untimed steps, then K timed steps between two device synchronisations. Each call is
-    also bracketed by a pair of events on the stream the kernels run on (torch's current
-    stream, which the binding passes to the library) for the per-launch duration."""
+def time_steps(step, steps: int, warmup: int, graph: bool = False):
+    """W untimed steps, then K timed steps between two device synchronisations.
+
+    The timed loop is bracketed by one pair of events on the stream the kernels run on (torch's
+    current stream, which the binding passes to the library); their elapsed time / K is the
+    per-launch duration used for the roofline. With graph=True one step is captured into a HIP
+    graph after the warmup and the loop replays it instead of calling the binding (on this
+    stack a graph launch costs more than the eager call it replaces for these single-kernel
+    steps, so eager calls are the default)."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        run = g.replay
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = sorted(a.elapsed_time(b) for a, b in ev)
-    mean = sum(per) / len(per)
+    mean = e0.elapsed_time(e1) / steps
     return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "launch_ms_mean": mean,
-            "launch_ms_median": per[len(per) // 2], "launch_ms_min": per[0]}
+            "graph": 1.0 if graph else 0.0}
 
 
 def load_traffic(kind: str, workload: str):
@@ -137,9 +152,9 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       f"query rows), float64 numpy, {t_total:.1f} s total"}
 
 
-def measure(w, steps, warmup, kind):
+def measure(w, steps, warmup, kind, graph=False):
     step = make_step(w)
-    t = time_steps(step, steps, warmup)
+    t = time_steps(step, steps, warmup, graph)
     if kind == "prefill":
         work = prefill_flops(w)
         achieved = work / (t["launch_ms_mean"] * 1e-3) / 1e12
@@ -164,6 +179,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph capturing one step instead of eager calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB, 5 times (reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -197,7 +214,7 @@ def main():
     w = w_cpu.to(dev) if w_cpu is not None else wl.make_config(head_c, device=dev)
     kind = w.kind
     log(f"[bench] timing {w.name}: warmup {args.warmup}, steps {args.steps}")
-    value, unit, roof, t, work = measure(w, args.steps, args.warmup, kind)
+    value, unit, roof, t, work = measure(w, args.steps, args.warmup, kind, args.graph)
     log(f"[bench] {w.name}: {value:.2f} {unit} per step, launch mean {t['launch_ms_mean']*1e3:.1f} us, "
         f"roofline frac {roof['frac']:.3f}")
 
@@ -230,7 +247,7 @@ def main():
                 continue
             log(f"[bench] config {c}: generating")
             wc = wl.make_config(c, device=dev)
-            v, u, rf, tc, wk = measure(wc, max(20, args.steps // 2), args.warmup, wc.kind)
+            v, u, rf, tc, wk = measure(wc, max(20, args.steps // 2), args.warmup, wc.kind, args.graph)
             log(f"[bench] {wc.name}: {v:.2f} {u}, launch mean {tc['launch_ms_mean']*1e3:.1f} us, frac {rf['frac']:.3f}")
             extra.append({"workload": wc.name, "value": round(v, 3), "unit": u,
                           "launch_us_mean": round(tc["launch_ms_mean"] * 1e3, 2),
