@@ -82,6 +82,9 @@ __device__ __forceinline__ void copy4_to_lds(const void* g, lds_void_t* lds_base
 // builtin, not inline asm, so the compiler's own wait insertion knows every earlier vector
 // memory operation, HBM->LDS copies included, has completed here.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(n) with expcnt and lgkmcnt at their no-wait maxima (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // Transposing LDS read: within each group of 16 lanes, lane i receives element (i % 4) of the
 // 4 bf16 values addressed by lane 4 * jj + i / 4, for jj = 0..3.

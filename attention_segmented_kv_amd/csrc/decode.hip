@@ -69,10 +69,6 @@ struct DecodeLayout {
   static constexpr int kCombFloats = kGroup * kHeadDim + 4 * kGroup;  // O^T, (m, l) of one wave
 };
 
-// s_waitcnt vmcnt(n) with expcnt and lgkmcnt at their no-wait maxima (gfx9 encoding: vmcnt
-// bits 3:0 and 15:14).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
 
