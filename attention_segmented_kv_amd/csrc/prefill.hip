@@ -419,11 +419,17 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
   __shared__ __attribute__((aligned(1024))) char lk0[kBlkBytes];
   __shared__ __attribute__((aligned(1024))) char lk1[kBlkBytes];
 
+  // Every pointer argument in scalar registers before the first table read, so that all
+  // kernel-argument loads share one memory round trip instead of being fetched as needed.
+  asm volatile("" ::"s"(q), "s"(k_pool), "s"(v_pool), "s"(segs), "s"(seg_indptr), "s"(cu_q),
+               "s"(cu_k), "s"(out), "s"(lse));
+
   // Work item: kv head fastest, so that with 8 kv heads every tile of head g lands on the same
-  // XCD (workgroups are dealt round-robin over the 8 XCDs) and shares its L2. Query tiles go heaviest (last) first;
-  // with fold > 0 (the whole grid resident at once, two workgroups per CU) the second half of
-  // the grid goes lightest first instead, so that the workgroups sharing a CU, dispatched
-  // one grid-half apart, have causal key counts that add up to about the same total.
+  // XCD (workgroups are dealt round-robin over the 8 XCDs) and shares its L2. Query tiles go
+  // heaviest (last) first; with fold > 0 (the whole grid resident at once, two workgroups per
+  // CU) the second half of the grid goes lightest first instead, so that the workgroups sharing
+  // a CU, dispatched one grid-half apart, have causal key counts that add up to about the same
+  // total.
   const int id = blockIdx.x;
   const int per_tile = hkv * batch;
   const int rank = id / per_tile;
@@ -431,26 +437,35 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
   const int rem = id % per_tile;
   const int b = rem / hkv;
   const int g = rem % hkv;
-  const int q0 = cu_q[b];
-  const int lq = cu_q[b + 1] - q0;
+  // The request's six table entries in one vector load (lanes 0-5), then broadcast: one
+  // memory round trip where scalar loads of the three tables would wait on each other.
+  int tv = 0;
+  {
+    const int tl = threadIdx.x & 63;
+    if (tl < 6) tv = (tl < 2 ? cu_q : (tl < 4 ? cu_k : seg_indptr))[b + (tl & 1)];
+  }
+  const int q0 = __builtin_amdgcn_readlane(tv, 0);
+  const int lq = __builtin_amdgcn_readlane(tv, 1) - q0;
+  const int K = __builtin_amdgcn_readlane(tv, 3) - __builtin_amdgcn_readlane(tv, 2);
+  const int seg_first = __builtin_amdgcn_readlane(tv, 4);
+  const int seg_last = __builtin_amdgcn_readlane(tv, 5);
   const int p0 = qtile * kPosPerTile;
   if (p0 >= lq) return;
-  const int K = cu_k[b + 1] - cu_k[b];
   const int hq = hkv * kGroup;
+  const int kfull = kCausal ? min(K, K - lq + p0 + 1) : K;  // keys every row sees
+  const int tend = kCausal ? min(K, K - lq + min(p0 + kPosPerTile, lq)) : K;
+  const int nblk = max(0, (tend + kBlockN - 1) / kBlockN);  // key blocks the tile sees
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int n = lane & 31;  // row within the wave
   const int h = lane >> 5;  // which half of the k / m slots this lane holds
-  const int pos = p0 + wave * 4 + (n >> 3);
   const int head = g * kGroup + (n & 7);
-  const bool row_valid = pos < lq;
 
-  const int last_pos = min(p0 + kPosPerTile - 1, lq - 1);
-  const int kend = kCausal ? min(K, K - lq + last_pos + 1) : K;  // keys the tile sees at all
-  const int kfull = kCausal ? min(K, K - lq + p0 + 1) : K;        // keys every row sees
-  const int n_blocks = max(0, (kend + kBlockN - 1) / kBlockN);
+  // Wave w holds positions p0 + 4w .. p0 + 4w + 3 of the tile.
+  const int pos = p0 + wave * 4 + (n >> 3);
+  const bool row_valid = pos < lq;
   const int row_limit = kCausal ? min(K, K - lq + pos + 1) : K;
 
   // Q fragments: B operand of S^T = K Q^T. Lane holds d = 16*step + 8*h + (0..7) of its row.
@@ -465,9 +480,10 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
   // ---- HBM -> LDS copies: 16 copy instructions of 1 KiB per block and tensor, four per wave.
   // K instruction c = 4 * wave + k fills rows 4c .. 4c + 3 (256 B each, swizzled: lane L holds
   // chunk (L % 16) ^ (row % 16) of row 4c + L / 16). V instruction c fills rows 16k .. 16k + 15
-  // of d quarter `wave` (64 B each): lane L copies 16 B of row 16k + L / 4.
+  // of d quarter `wave` (64 B each): lane L copies 16 B of row 16k + L / 4. Each wave writes
+  // only bytes [4096 w, 4096 w + 4096) of every K and V slot.
   BlockCursor cur;
-  cur.init(segs, seg_indptr[b], seg_indptr[b + 1]);
+  cur.init(segs, seg_first, seg_last);
   const int64_t tok_stride = (int64_t)hkv * kHeadDim;
   const uint32_t tok_bytes = (uint32_t)hkv * kHeadDim * 2;
   const bf16_t* kbase = k_pool + (int64_t)g * kHeadDim;
@@ -638,44 +654,61 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
     }
   };
 
-  // Block j lives in slot j & 1; the copies of block j + 1 go to the other slot, which every
-  // wave finished reading before the barrier that ended step j - 1.
-  if (n_blocks > 0) {
+  // ---- normalise and store the tile's rows. O^T column n is row n of the wave
+  // (lane holds d = 32 dt + 8 k4 + 4 h + (0..3)); the rows go through the wave's own 8 KiB of
+  // an LDS slot nobody reads any more (rows 0-15 in its K part, 16-31 in its V part, 16-byte
+  // chunk c of row r at chunk position c ^ (r % 16)) and leave it as whole 256-byte rows: each
+  // store instruction writes 4 heads of one position, 1 KiB contiguous.
+  auto store_rows = [&](char* kslot, char* vslot) __attribute__((always_inline)) {
+    const float l_tot = sum_xor32(l_run);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    lds_char_t* wk = (lds_char_t*)kslot + wave * 4096;
+    lds_char_t* wv = (lds_char_t*)vslot + wave * 4096;
+    lds_char_t* wrow = (n < 16 ? wk : wv) + (n & 15) * 256 + 8 * h;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        bf16x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (bf16_t)(o[dt][4 * k4 + t] * inv);
+        *(lds_bf16x4_t*)(wrow + (((4 * dt + k4) ^ (n & 15)) << 4)) = v;
+      }
+    }
+    if (lse != nullptr && h == 0 && row_valid)
+      lse[(int64_t)(q0 + pos) * hq + head] = l_tot > 0.f ? m_run * scale + __logf(l_tot) : -INFINITY;
+    const int rr = lane >> 4, cc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * (i & 3) + rr;  // row within its 16-row half
+      const bf16x8 v = lds_read16((i < 4 ? wk : wv) + r * 256 + ((cc ^ r) << 4));
+      const int ps = p0 + wave * 4 + (i >> 1);
+      if (ps < lq)
+        *reinterpret_cast<bf16x8*>(out + ((int64_t)(q0 + ps) * hq + g * kGroup + 4 * (i & 1) + rr) * kHeadDim +
+                                   8 * cc) = v;
+    }
+  };
+
+  // Block j runs from slot j & 1; the copies of block j + 1 go to the other slot, which every
+  // wave finished reading before the barrier that ended the step before.
+  if (nblk > 0) {
     issue_copies(0, lk0, lv0);
     wait_vmem();  // also the Q loads
     phase_barrier();
-    for (int j = 0; j < n_blocks; j += 2) {
-      if (j + 1 < n_blocks) issue_copies(j + 1, lk1, lv1);
+    for (int j = 0; j < nblk; j += 2) {
+      if (j + 1 < nblk) issue_copies(j + 1, lk1, lv1);
       block_step(j, lk0, lv0);
       wait_vmem();
       phase_barrier();
-      if (j + 1 >= n_blocks) break;
-      if (j + 2 < n_blocks) issue_copies(j + 2, lk0, lv0);
+      if (j + 1 >= nblk) break;
+      if (j + 2 < nblk) issue_copies(j + 2, lk0, lv0);
       block_step(j + 1, lk1, lv1);
       wait_vmem();
       phase_barrier();
     }
   }
-
-  // ---- normalise and store: O row = O^T column n; lane holds d = 32 dt + 8 (e / 4) + 4 h + e % 4
-  const float l_tot = sum_xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (row_valid) {
-    bf16_t* orow = out + ((int64_t)(q0 + pos) * hq + head) * kHeadDim;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const int d = 32 * dt + 8 * k4 + 4 * h;
-        bf16x4 v;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = (bf16_t)(o[dt][4 * k4 + t] * inv);
-        *reinterpret_cast<bf16x4*>(orow + d) = v;
-      }
-    }
-    if (lse != nullptr && h == 0)
-      lse[(int64_t)(q0 + pos) * hq + head] = l_tot > 0.f ? m_run * scale + __logf(l_tot) : -INFINITY;
-  }
+  // every wave is past the last barrier: all slots are free
+  store_rows(lk0, lv0);
 }
 
 }  // namespace
