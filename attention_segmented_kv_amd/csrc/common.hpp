@@ -78,6 +78,15 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, lds_void_t* lds_bas
 __device__ __forceinline__ void copy4_to_lds(const void* g, lds_void_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, lds_base, 4, 0, 0);
 }
+// The same two copies marked non-temporal (the nt cache-policy bit), for data read exactly once
+// in a stream. Measured on the decode read pattern (a kv head's 256-byte slices of consecutive
+// pool rows): about 6.8 TB/s with the bit against 6.0 TB/s without.
+__device__ __forceinline__ void copy16_to_lds_stream(const void* g, lds_void_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 2);
+}
+__device__ __forceinline__ void copy4_to_lds_stream(const void* g, lds_void_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 4, 0, 2);
+}
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their "no wait" maxima). Issued through the
 // builtin, not inline asm, so the compiler's own wait insertion knows every earlier vector
 // memory operation, HBM->LDS copies included, has completed here.

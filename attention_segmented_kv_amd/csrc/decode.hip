@@ -598,8 +598,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         vc = kc;
       }
       const int64_t row = slot_of[i] * tok_bytes;
-      copy16_to_lds(kbase + row + kc * 16, (lds_void_t*)(kb + i * 1024));
-      copy16_to_lds(vbase + row + vc * 16, (lds_void_t*)(vb + i * 1024));
+      copy16_to_lds_stream(kbase + row + kc * 16, (lds_void_t*)(kb + i * 1024));
+      copy16_to_lds_stream(vbase + row + vc * 16, (lds_void_t*)(vb + i * 1024));
     }
     if constexpr (kFp8 == 1) {
       // scales: lane L copies those of row L
