@@ -236,6 +236,7 @@ constexpr int kBuckets = 256;
 // the plan costs few memory latencies.
 // hdr[0] = len, hdr[1] = number of chunks listed (0 if they would not fit in max_chunks).
 constexpr int kPlanSegs = 8;  // segments per request read up front
+constexpr int kSpreadMax = 512;  // plan: batches up to this size share each request's chunks
 
 // Inclusive scan over the 1024 threads of the block of two counts at once: shuffles within each
 // wave, then one pass over the 16 wave totals. wtot is LDS scratch of 2 x 16 ints.
@@ -291,6 +292,11 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
   __shared__ int wtot[32];
   __shared__ int hist[kBuckets], bucket_base[kBuckets], bucket_fill[kBuckets];
   __shared__ int carry_n, carry_f;
+  // batches of at most kSpreadMax requests: each request's scan results and first segments,
+  // for the threads that share its chunks in pass 2
+  __shared__ int rq_first[kSpreadMax], rq_ffirst[kSpreadMax], rq_n[kSpreadMax], rq_f[kSpreadMax];
+  __shared__ int rq_K[kSpreadMax], rq_sa[kSpreadMax], rq_se[kSpreadMax];
+  __shared__ Segment rq_sg[kSpreadMax * kPlanSegs];
   const int tid = threadIdx.x;
   // This thread's request in the first block, read once and kept for both passes. Every load
   // is unconditional, at an index clamped into its table, so that they are all in flight at
@@ -358,7 +364,61 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
     if (tid < kBuckets) bucket_base[kBuckets - 1 - tid] = total_f + hcount - hist[kBuckets - 1 - tid];
   }
   __syncthreads();
-  // pass 2: chunk offsets and records
+  // pass 2: chunk offsets and records. The record of chunk k of request b: its schedule
+  // position (full chunks in request order, then the short last ones by decreasing length) and
+  // the segment cursor at its first key, found by walking the request's segments in key order.
+  auto write_rec = [&](int b, int k, int K, int n, int f, int first, int ffirst, int idx, int se,
+                       int start, const Segment& sg) __attribute__((always_inline)) {
+    const int kbeg = k * len;
+    int pos = ffirst + k;
+    if (k >= f) {
+      const int bk = (int)((int64_t)(K - f * len) * kBuckets / len);
+      pos = bucket_base[bk] + atomicAdd(&bucket_fill[bk], 1);
+    }
+    if (pos < max_chunks && first + k < max_chunks) {
+      i32x4* r = reinterpret_cast<i32x4*>(recs + (int64_t)pos * kRecInts);
+      r[0] = i32x4{b, kbeg, min(K, kbeg + len), n == 1 ? 1 : 0};
+      r[1] = i32x4{idx, se, start, sg.pool_offset};
+      r[2] = i32x4{sg.length, first + k, 0, 0};
+    }
+  };
+  if (batch <= kSpreadMax) {
+    // One block of requests (pass 1 ran once): tpr threads per request take its chunks
+    // k = kq, kq + tpr, ..., so that long requests (hundreds of chunks) are not written by one
+    // thread in sequence.
+    int tpr = 1;
+    while (tpr < 64 && batch * tpr * 2 <= 1024) tpr *= 2;
+    if (tid < batch) {
+      rq_first[tid] = sn0 - n0;
+      rq_ffirst[tid] = sf0 - f0;
+      rq_n[tid] = n0;
+      rq_f[tid] = f0;
+      rq_K[tid] = K0;
+      rq_sa[tid] = s0;
+      rq_se[tid] = s1;
+#pragma unroll
+      for (int j = 0; j < kPlanSegs; ++j) rq_sg[tid * kPlanSegs + j] = sg0[j];
+    }
+    __syncthreads();
+    const int b = tid / tpr, kq = tid - b * tpr;
+    if (b < batch) {
+      const int K = rq_K[b], n = rq_n[b], f = rq_f[b], first = rq_first[b], ffirst = rq_ffirst[b];
+      const int sa = rq_sa[b], se = rq_se[b];
+      if (kq == 0) chunk_base[b] = first;
+      int idx = sa, start = 0;
+      Segment sg = rq_sg[b * kPlanSegs];
+      for (int k = kq; k < n; k += tpr) {
+        const int kbeg = k * len;
+        while (idx < se && kbeg - start >= sg.length) {
+          start += sg.length;
+          ++idx;
+          const int j = idx - sa;
+          sg = j < kPlanSegs ? rq_sg[b * kPlanSegs + j] : (idx < se ? segs[idx] : Segment{0, 0x7fffffff});
+        }
+        write_rec(b, k, K, n, f, first, ffirst, idx, se, start, sg);
+      }
+    }
+  } else {
   int cn = 0, cf = 0;  // chunks and full chunks of the blocks before
   for (int b0 = 0; b0 < batch; b0 += 1024) {
     const int b = b0 + tid;
@@ -404,17 +464,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
             sg = idx < se ? segs[idx] : Segment{0, 0x7fffffff};
           }
         }
-        int pos = ffirst + k;
-        if (k >= f) {
-          const int bk = (int)((int64_t)(K - f * len) * kBuckets / len);
-          pos = bucket_base[bk] + atomicAdd(&bucket_fill[bk], 1);
-        }
-        if (pos < max_chunks && first + k < max_chunks) {
-          i32x4* r = reinterpret_cast<i32x4*>(recs + (int64_t)pos * kRecInts);
-          r[0] = i32x4{b, kbeg, min(K, kbeg + len), n == 1 ? 1 : 0};
-          r[1] = i32x4{idx, se, start, sg.pool_offset};
-          r[2] = i32x4{sg.length, first + k, 0, 0};
-        }
+        write_rec(b, k, K, n, f, first, ffirst, idx, se, start, sg);
       }
     }
     // totals of this block for the next one (the last thread holds the block's inclusive sums)
@@ -428,6 +478,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
       cn = carry_n;
       cf = carry_f;
     }
+  }
   }
   if (tid == 0) {
     chunk_base[batch] = total_n;

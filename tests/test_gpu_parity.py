@@ -169,6 +169,19 @@ def test_decode_ragged_full(case):
     _full_compare(w, f"ragged-decode-{seed}", num_splits=ns)
 
 
+@needs_gpu
+@pytest.mark.parametrize("batch,kvd", [(512, "bf16"), (513, "bf16"), (700, "fp8_e4m3")])
+def test_decode_large_batches(batch, kvd):
+    """The decode plan spreads each request's chunks over several threads up to 512 requests and
+    walks them one thread per request above that: both sides of the boundary, short requests in
+    up to 3 segments, the chunk length forced small so that most requests have several chunks."""
+    print(f"[case] large-batch decode B={batch} {kvd}", flush=True)
+    kl = [int(x) for x in np.random.default_rng(40 + batch).integers(1, 200, size=batch)]
+    w = wl.make_random(40 + batch, batch=batch, q_lens=[1] * batch, k_lens=kl, max_segs=3,
+                       kv_dtype=kvd, kind="decode").to("cuda")
+    _full_compare(w, f"decode-B{batch}", num_splits=4)
+
+
 # ---------------------------------------------------------------- invariants on the device
 
 @needs_gpu
