@@ -6,6 +6,8 @@ import this package. It shares no code with the HIP library.
 from .attention import (attend, attention, attention_rows, bf16_to_f64, decode_kv,
                         e4m3fn_to_f64, merge_partials, request_slots, split_merge,
                         visible_keys)
+from .kv_append import bf16_bits_to_f32, f32_to_e4m3fn, kv_append, quantize_rows
 
-__all__ = ["attend", "attention", "attention_rows", "bf16_to_f64", "decode_kv", "e4m3fn_to_f64",
-           "merge_partials", "request_slots", "split_merge", "visible_keys"]
+__all__ = ["attend", "attention", "attention_rows", "bf16_bits_to_f32", "bf16_to_f64", "decode_kv",
+           "e4m3fn_to_f64", "f32_to_e4m3fn", "kv_append", "merge_partials", "quantize_rows",
+           "request_slots", "split_merge", "visible_keys"]

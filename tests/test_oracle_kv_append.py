@@ -1,0 +1,123 @@
+"""Pins of the KV-append oracle (CPU): the E4M3FN encoder against torch's float8 conversion,
+every code and hand-worked ties; the row quantiser's scale and extremes; the append against
+what it must leave in the pool, read back through the segment tables."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _torch_e4m3fn(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_encoder_matches_torch_on_random_values():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        (rng.standard_normal(100_000) * 100).clip(-448, 448),
+        rng.standard_normal(50_000) * 0.01,        # subnormal codes
+        rng.uniform(-448, 448, 50_000),
+    ]).astype(np.float32)
+    assert np.array_equal(oracle.f32_to_e4m3fn(x), _torch_e4m3fn(x))
+
+
+def test_encoder_round_trips_every_finite_code():
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]  # 0x7F, 0xFF are NaN
+    vals = oracle.e4m3fn_to_f64(codes).astype(np.float32)
+    vals = np.where(codes == 0x80, np.float32(-0.0), vals)
+    assert np.array_equal(oracle.f32_to_e4m3fn(vals), codes)
+
+
+def test_encoder_ties_go_to_even_codes():
+    # hand-worked: 1.0 = 0x38 and 1.125 = 0x39, so 1.0625 -> 0x38; 1.1875 lies between 0x39 and
+    # 1.25 = 0x3A -> 0x3A; 2^-10 is half the smallest subnormal 2^-9 -> 0; 3 * 2^-10 lies between
+    # 2^-9 (0x01) and 2^-8 (0x02) -> 0x02; 432 lies between 416 (0x7D) and 448 (0x7E) -> 0x7E
+    x = np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 432.0, -1.0625], dtype=np.float32)
+    assert oracle.f32_to_e4m3fn(x).tolist() == [0x38, 0x3A, 0x00, 0x02, 0x7E, 0xB8]
+    # every midpoint between adjacent positive codes, and torch agrees
+    pos = np.arange(0, 0x7F, dtype=np.uint8)
+    v = oracle.e4m3fn_to_f64(pos)
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    enc = oracle.f32_to_e4m3fn(mids)
+    assert np.all(enc % 2 == 0)
+    assert np.array_equal(enc, _torch_e4m3fn(mids))
+
+
+def test_encoder_error_is_at_most_half_a_step():
+    rng = np.random.default_rng(1)
+    x = rng.uniform(-448, 448, 20_000).astype(np.float32)
+    dec = oracle.e4m3fn_to_f64(oracle.f32_to_e4m3fn(x))
+    a = np.abs(x.astype(np.float64))
+    step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+    assert np.all(np.abs(dec - x) <= step / 2)
+
+
+def test_quantize_rows_scale_extremes_and_zero_rows():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((64, 8, 128)).astype(np.float32)
+    x[3, 5] = 0.0
+    codes, scale = oracle.quantize_rows(x)
+    amax = np.abs(x).max(axis=-1)
+    expect = np.where(amax > 0, amax / np.float32(448), np.float32(1)).astype(np.float32)
+    assert np.array_equal(scale, expect)
+    assert scale[3, 5] == 1.0 and not codes[3, 5].any()
+    # the largest-magnitude element of a nonzero row encodes as +-448 (0x7E / 0xFE)
+    idx = np.abs(x).argmax(axis=-1)
+    top = np.take_along_axis(codes, idx[..., None], axis=-1)[..., 0]
+    nz = amax > 0
+    assert np.all((top[nz] & 0x7F) == 0x7E)
+    # decoded rows are within half a code step of the input: at most 16 code units (the step is
+    # 32 in the top binade, 256..448) times the stored scale; exact ties reach the bound
+    dec = oracle.e4m3fn_to_f64(codes) * scale[..., None]
+    assert np.all(np.abs(dec - x) <= scale[..., None].astype(np.float64) * 16.0 * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3"])
+def test_kv_append_writes_the_last_keys_and_nothing_else(fmt):
+    gen = torch.Generator().manual_seed(3)
+    # four requests with segments (one with none), new tokens at the end of each
+    w = wl.make_random(3, batch=4, q_lens=[1] * 4, k_lens=[50, 0, 130, 7], max_segs=4, kind="decode",
+                       kv_dtype=fmt, zero_length_segments=True)
+    segs, ind, _, ck = wl.host_tables(w)
+    n_new = [5, 0, 130, 1]
+    cu_new = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int64)
+    T, hkv, d = int(cu_new[-1]), 8, 128
+    k_new = wl.bits(torch.randn(T, hkv, d, generator=gen).to(torch.bfloat16))
+    v_new = wl.bits(torch.randn(T, hkv, d, generator=gen).to(torch.bfloat16))
+    kp0, vp0 = wl.bits(w.k_pool), wl.bits(w.v_pool)
+    ks0 = None if w.k_scale is None else w.k_scale.numpy().copy()
+    vs0 = None if w.v_scale is None else w.v_scale.numpy().copy()
+    kp, vp, ks, vs = oracle.kv_append(k_new, v_new, segs, ind, cu_new, ck, kp0, vp0, ks0, vs0, fmt=fmt)
+    touched = np.zeros(kp0.shape[0], dtype=bool)
+    for b in range(4):
+        K, n = int(ck[b + 1] - ck[b]), n_new[b]
+        slots = oracle.request_slots(segs, ind, b)[K - n:]
+        touched[slots] = True
+        src = slice(int(cu_new[b]), int(cu_new[b + 1]))
+        if fmt == "bf16":
+            assert np.array_equal(kp[slots], k_new[src]) and np.array_equal(vp[slots], v_new[src])
+        else:
+            for pool, sc, new in ((kp, ks, k_new), (vp, vs, v_new)):
+                x = oracle.bf16_to_f64(new[src])
+                amax = np.abs(x).max(axis=-1)
+                assert np.array_equal(sc[slots], np.where(amax > 0, amax.astype(np.float32) / np.float32(448), 1))
+                dec = oracle.e4m3fn_to_f64(pool[slots]) * sc[slots][..., None]
+                assert np.all(np.abs(dec - x) <= sc[slots][..., None].astype(np.float64) * 16.0 * (1 + 1e-6))
+    # every other slot (and scale) is left as it was
+    assert np.array_equal(kp[~touched], kp0[~touched]) and np.array_equal(vp[~touched], vp0[~touched])
+    if fmt != "bf16":
+        assert np.array_equal(ks[~touched], ks0[~touched], equal_nan=True)
+        assert np.array_equal(vs[~touched], vs0[~touched], equal_nan=True)
+
+
+def test_kv_append_rejects_more_new_tokens_than_keys():
+    w = wl.make_random(4, batch=1, q_lens=[1], k_lens=[3], max_segs=1, kind="decode")
+    segs, ind, _, ck = wl.host_tables(w)
+    z = np.zeros((4, 8, 128), dtype=np.uint16)
+    with pytest.raises(ValueError):
+        oracle.kv_append(z, z, segs, ind, [0, 4], ck, wl.bits(w.k_pool), wl.bits(w.v_pool))
