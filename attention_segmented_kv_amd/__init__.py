@@ -8,6 +8,8 @@ kernels. If the library has not been built, every call raises.
                   max_seqlen_q, max_seqlen_k, causal=True)
     out = decode(q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_k, max_seqlen_k,
                  k_scale=None, v_scale=None)
+    kv_append(k_new, v_new, segs, seg_indptr, cu_seqlens_new, cu_seqlens_k, k_pool, v_pool,
+              k_scale=None, v_scale=None)
 """
 from __future__ import annotations
 
@@ -18,7 +20,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "decode", "decode_num_splits", "decode_workspace_bytes", "validate_tables",
+__all__ = ["prefill", "decode", "kv_append", "decode_num_splits", "decode_workspace_bytes", "validate_tables",
            "status_string", "version", "library_path", "SegAttnError", "KV_BF16", "KV_FP8_E4M3"]
 
 KV_BF16 = 0
@@ -58,6 +60,8 @@ def _load():
     lib.seg_attn_decode_workspace_bytes.restype = SZ
     lib.seg_attn_decode_num_splits.argtypes = [I32, I32, I32, I32, I32, ctypes.POINTER(I32)]
     lib.seg_attn_decode_num_splits.restype = I32
+    lib.seg_attn_kv_append.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I64, I32, P, P, P, P, P]
+    lib.seg_attn_kv_append.restype = I32
     lib.seg_attn_status_string.argtypes = [I32]
     lib.seg_attn_status_string.restype = ctypes.c_char_p
     lib.seg_attn_validate_tables.argtypes = [P, I64, P, P, P, I32, I64, I32, ctypes.POINTER(I64)]
@@ -234,6 +238,55 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: to
     if st != 0:
         raise SegAttnError("seg_attn_decode", st)
     return (out, lse) if return_lse else out
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, segs: torch.Tensor, seg_indptr: torch.Tensor,
+              cu_seqlens_new: torch.Tensor, cu_seqlens_k: torch.Tensor, k_pool: torch.Tensor,
+              v_pool: torch.Tensor, *, k_scale: Optional[torch.Tensor] = None,
+              v_scale: Optional[torch.Tensor] = None) -> None:
+    """Write new tokens into their requests' segments, in place; see seg_attn_kv_append.
+
+    k_new/v_new [total_new, Hkv, 128] bf16; segs/seg_indptr/cu_seqlens_k describe the requests
+    after the append (their last n_b keys are the new tokens); cu_seqlens_new [B+1] int32.
+    A bf16 pool gets the rows as they are; a float8_e4m3fn pool gets per-row scaled codes and
+    k_scale/v_scale [pool_tokens, Hkv] fp32 the scales."""
+    lib = _load()
+    dev = k_new.device
+    if dev.type != "cuda":
+        raise ValueError("k_new must be a GPU tensor")
+    _check(k_new, "k_new", (torch.bfloat16,), dev, 3)
+    _check(v_new, "v_new", (torch.bfloat16,), dev, 3)
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must have the same shape")
+    fp8 = k_pool.dtype == torch.float8_e4m3fn
+    kv_types = (torch.float8_e4m3fn,) if fp8 else (torch.bfloat16,)
+    _check(k_pool, "k_pool", kv_types, dev, 3)
+    _check(v_pool, "v_pool", kv_types, dev, 3)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape")
+    total_new, hkv, d = k_new.shape
+    pool_tokens = k_pool.shape[0]
+    if tuple(k_pool.shape[1:]) != (hkv, d):
+        raise ValueError("k_new rows and pool rows differ in shape")
+    batch = cu_seqlens_new.shape[0] - 1
+    _check_tables(segs, seg_indptr, (cu_seqlens_new, cu_seqlens_k), dev, batch + 1,
+                  ("segs", "seg_indptr", "cu_seqlens_new", "cu_seqlens_k"))
+    if fp8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("an fp8 pool needs k_scale and v_scale")
+        for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _check(t, nm, (torch.float32,), dev, 2)
+            if tuple(t.shape) != (pool_tokens, hkv):
+                raise ValueError(f"{nm} must have shape [pool_tokens, Hkv]")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.seg_attn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(segs), _ptr(seg_indptr),
+                                    _ptr(cu_seqlens_new), _ptr(cu_seqlens_k), batch, total_new, hkv, d,
+                                    pool_tokens, KV_FP8_E4M3 if fp8 else KV_BF16, _ptr(k_pool),
+                                    _ptr(v_pool), _ptr(k_scale if fp8 else None),
+                                    _ptr(v_scale if fp8 else None), stream)
+    if st != 0:
+        raise SegAttnError("seg_attn_kv_append", st)
 
 
 def validate_tables(segs, seg_indptr, cu_seqlens_k, pool_tokens: int, *, cu_seqlens_q=None,

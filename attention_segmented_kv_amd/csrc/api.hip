@@ -21,6 +21,11 @@ hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          int forced_len, int min_len, int max_chunks, int cu_count, float scale,
                          void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* recs,
                          float* ws_o, float* ws_lse, hipStream_t stream);
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const void* segs,
+                            const int32_t* seg_indptr, const int32_t* cu_new, const int32_t* cu_k,
+                            int batch, int total_new, int hkv, int64_t pool_tokens, int fp8,
+                            void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                            hipStream_t stream);
 }  // namespace segattn
 
 namespace {
@@ -216,6 +221,41 @@ seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void*
         num_heads_kv, p.forced_len, p.min_len, (int)max_chunks, current_cu_count(), softmax_scale, out,
         lse, (int32_t*)ws, (int32_t*)(ws + lay.base), (int32_t*)(ws + lay.tab), (float*)(ws + lay.o),
         (float*)(ws + lay.lse), (hipStream_t)stream);
+    return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
+  } catch (...) {
+    return SEG_ATTN_ERR_HIP;
+  }
+}
+
+seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
+                                     const seg_attn_segment_t* segs, const int32_t* seg_indptr,
+                                     const int32_t* cu_seqlens_new, const int32_t* cu_seqlens_k,
+                                     int32_t batch, int32_t total_new, int32_t num_heads_kv,
+                                     int32_t head_dim, int64_t pool_tokens, int32_t kv_dtype,
+                                     void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                     seg_attn_stream_t stream) {
+  try {
+    if (batch < 0 || total_new < 0 || pool_tokens < 0 || num_heads_kv <= 0 || head_dim <= 0)
+      return SEG_ATTN_ERR_INVALID_ARG;
+    if (kv_dtype != SEG_ATTN_KV_BF16 && kv_dtype != SEG_ATTN_KV_FP8_E4M3) return SEG_ATTN_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim) return SEG_ATTN_ERR_UNSUPPORTED;
+    if (pool_tokens > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
+    if (batch == 0 && total_new > 0) return SEG_ATTN_ERR_INVALID_ARG;
+    if (batch == 0 || total_new == 0) return SEG_ATTN_OK;
+    const bool fp8 = kv_dtype == SEG_ATTN_KV_FP8_E4M3;
+    if (!k_new || !v_new || !segs || !seg_indptr || !cu_seqlens_new || !cu_seqlens_k || !k_pool || !v_pool)
+      return SEG_ATTN_ERR_INVALID_ARG;
+    if (fp8 && (!k_scale || !v_scale)) return SEG_ATTN_ERR_INVALID_ARG;
+    // rows move as 16-byte (bf16) or 8-byte (FP8 codes) pieces, scales as 4-byte words
+    auto misaligned = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
+    if (misaligned(k_new, 16) || misaligned(v_new, 16) || misaligned(k_pool, fp8 ? 8 : 16) ||
+        misaligned(v_pool, fp8 ? 8 : 16) || (fp8 && (misaligned(k_scale, 4) || misaligned(v_scale, 4))))
+      return SEG_ATTN_ERR_INVALID_ARG;
+    if ((int64_t)total_new * num_heads_kv > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
+    hipError_t e = segattn::launch_kv_append(k_new, v_new, segs, seg_indptr, cu_seqlens_new,
+                                             cu_seqlens_k, batch, total_new, num_heads_kv,
+                                             pool_tokens, fp8 ? 1 : 0, k_pool, v_pool, k_scale,
+                                             v_scale, (hipStream_t)stream);
     return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
   } catch (...) {
     return SEG_ATTN_ERR_HIP;

@@ -1,0 +1,227 @@
+// KV append: a batch's new tokens' K and V rows written into their requests' segments, the step
+// ahead of attention. Each request's cache is a few contiguous segments of one shared pool
+// (Flood README, "Introduction"); the FP8 variant quantises on write, one fp32 scale per
+// (token, kv head) row, for the FP8 KV cache of the same README's feature list.
+//
+// Request b appends n_b = cu_new[b+1] - cu_new[b] tokens and cu_k counts its keys after the
+// append, so its new tokens are its last n_b keys, logical positions K_b - n_b .. K_b - 1.
+//
+// One 16-lane group per (token, kv head) row of 128 values, 16 rows per 256-thread workgroup.
+// The group loads its row (8 values per lane, 16-byte pieces), finds the token's request and
+// the key's pool slot with its lanes working together on the tables, and stores the row there.
+// The FP8 row scale is max|x| / 448 (1 for an all-zero row); each value is divided by it in
+// fp32, correctly rounded, and converted to E4M3FN by the hardware conversion (round to
+// nearest, ties to even) after a clamp to +-448.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace segattn {
+
+namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Seg {
+  int32_t off, len;
+};
+
+constexpr int kRowsPerBlock = 16;
+constexpr float kFp8Max = 448.0f;
+
+// float pair -> two E4M3FN bytes in the low half of a word (hardware conversion, RNE)
+__device__ __forceinline__ uint32_t pack_fp8x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// x / s correctly rounded, from r = 1/s correctly rounded: q = x r, then two corrections
+// q += (x - q s) r, each residual exact in an fma. After the first correction q is within one
+// ulp of x / s, and then the residual step rounds correctly (Markstein's theorem on division by
+// a correctly rounded reciprocal; it needs no underflow in the residuals, which the callers'
+// range of s, 2^-80 .. 2^80, ensures for every quotient of magnitude 2^-11 or more, and smaller
+// quotients encode as a signed zero either way). The sign is taken from x so that x = -0
+// keeps its sign.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+  float q = __fmul_rn(x, r);
+  q = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+  q = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+  return __builtin_copysignf(q, x);
+}
+
+// Lane data movement inside the 16-lane DPP rows, which are the row groups: kCtrl is a DPP
+// control (quad_perm 0x00-0xFF, row_shr 0x111-0x11F, row_mirror 0x140, row_half_mirror 0x141).
+// A lane whose source lies outside its row reads 0.
+template <int kCtrl>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+
+// Maximum over the 16 lanes of a row group of non-negative floats (their bit patterns order
+// like the values): swap neighbours, then pairs, then quads (half-row mirror), then halves.
+__device__ __forceinline__ float group_max_nonneg(float v) {
+  int b = __builtin_bit_cast(int, v);
+  b = max(b, dpp<0xB1>(b));   // quad_perm [1, 0, 3, 2]
+  b = max(b, dpp<0x4E>(b));   // quad_perm [2, 3, 0, 1]
+  b = max(b, dpp<0x141>(b));  // row_half_mirror
+  b = max(b, dpp<0x140>(b));  // row_mirror
+  return __builtin_bit_cast(float, b);
+}
+
+// Inclusive prefix sum over the 16 lanes of a row group.
+__device__ __forceinline__ int group_inclusive_sum(int v) {
+  v += dpp<0x111>(v);  // row_shr 1
+  v += dpp<0x112>(v);  // row_shr 2
+  v += dpp<0x114>(v);  // row_shr 4
+  v += dpp<0x118>(v);  // row_shr 8
+  return v;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 raw, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __builtin_bit_cast(float, raw[i] << 16);
+    x[2 * i + 1] = __builtin_bit_cast(float, raw[i] & 0xFFFF0000u);
+  }
+}
+
+// Eight quotients, clamped to +-448, as E4M3FN codes (byte i = value i).
+__device__ __forceinline__ u32x2 encode_fp8x8(const float (&y)[8]) {
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = fminf(fmaxf(y[4 * i + q], -kFp8Max), kFp8Max);
+    w[i] = pack_fp8x2(c[0], c[1]) | (pack_fp8x2(c[2], c[3]) << 16);
+  }
+  return u32x2{w[0], w[1]};
+}
+
+// Mask of the calling lane's 16-lane group (bit i = group lane i) of a predicate.
+__device__ __forceinline__ uint32_t group_ballot(bool p) {
+  const int shift = __lane_id() & 48;
+  return (uint32_t)(__ballot(p) >> shift) & 0xFFFFu;
+}
+
+template <bool kFp8>
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const Seg* __restrict__ segs, const int32_t* __restrict__ seg_indptr,
+    const int32_t* __restrict__ cu_new, const int32_t* __restrict__ cu_k, int batch, int total_new,
+    int hkv, int64_t pool_tokens, void* __restrict__ k_pool, void* __restrict__ v_pool,
+    float* __restrict__ k_scale, float* __restrict__ v_scale) {
+  // rows number fewer than 2^31 (checked by the caller), so 32-bit index arithmetic suffices
+  const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  if (row >= (uint32_t)total_new * (uint32_t)hkv) return;  // whole 16-lane groups leave together
+  const int sub = threadIdx.x & 15;                         // values 8 sub .. 8 sub + 7 of the row
+  const int t = (int)(row / (uint32_t)hkv);
+  const int h = (int)(row - (uint32_t)t * (uint32_t)hkv);
+
+  // the row's values are loaded first: they do not depend on where the row goes
+  const int64_t src = (int64_t)row * 128 + 8 * sub;
+  const u32x4 kraw = *reinterpret_cast<const u32x4*>(k_new + src);
+  const u32x4 vraw = *reinterpret_cast<const u32x4*>(v_new + src);
+
+  // Request of token t: the largest b with cu_new[b] <= t (requests without new tokens have
+  // cu_new[b] == cu_new[b + 1] and are passed over). The group's 16 lanes probe 16 evenly
+  // spaced entries of [lo, hi) at once, which shrinks the range 16-fold per step: one step for
+  // up to 17 requests, two for up to 257.
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 14) >> 4;  // ceil((hi - lo - 1) / 16)
+    const int idx = lo + (sub + 1) * step;
+    const uint32_t le = group_ballot(idx < hi && cu_new[idx] <= t);  // a prefix of the lanes
+    const int c = __popc(le);
+    hi = min(hi, lo + (c + 1) * step);
+    lo += c * step;
+  }
+  const int b = lo;
+  const int n0 = cu_new[b], n1 = cu_new[b + 1];
+  const int j = (cu_k[b + 1] - cu_k[b]) - (n1 - n0) + (t - n0);  // logical key of token t
+  const int seg_end = seg_indptr[b + 1];
+
+  // Its pool slot: the group reads 16 of the request's segments at once, and the lane whose
+  // key range [start, start + len) holds j gives the slot (empty segments hold nothing).
+  int64_t slot = -1;
+  int before = 0;  // keys in the request's segments ahead of this batch of 16
+  for (int first = seg_indptr[b]; first < seg_end; first += 16) {
+    const int idx = first + sub;
+    const Seg sg = idx < seg_end ? segs[idx] : Seg{0, 0};
+    const int incl = group_inclusive_sum(sg.len);
+    const int start = before + incl - sg.len;
+    const uint32_t hit = group_ballot(j >= start && j < before + incl);
+    if (hit != 0) {
+      const int src_lane = __ffs(hit) - 1;
+      slot = (int64_t)__shfl(sg.off, src_lane, 16) + (j - __shfl(start, src_lane, 16));
+      break;
+    }
+    before += __shfl(incl, 15, 16);
+  }
+  // a key outside the request's segments or the pool means inconsistent tables: nothing is
+  // written for it rather than a write out of bounds
+  if (j < 0 || slot < 0 || slot >= pool_tokens) return;
+
+  const int64_t dst_row = slot * hkv + h;
+  if constexpr (!kFp8) {
+    __builtin_nontemporal_store(kraw, reinterpret_cast<u32x4*>((uint16_t*)k_pool + dst_row * 128 + 8 * sub));
+    __builtin_nontemporal_store(vraw, reinterpret_cast<u32x4*>((uint16_t*)v_pool + dst_row * 128 + 8 * sub));
+  } else {
+    // K and V rows side by side: row maxima over the group, scales, quotients, codes
+    float xk[8], xv[8];
+    unpack_bf16x8(kraw, xk);
+    unpack_bf16x8(vraw, xv);
+    float ak = 0.f, av = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ak = fmaxf(ak, fabsf(xk[i]));
+      av = fmaxf(av, fabsf(xv[i]));
+    }
+    ak = group_max_nonneg(ak);
+    av = group_max_nonneg(av);
+    const float sk = ak > 0.f ? ak / kFp8Max : 1.0f;
+    const float sv = av > 0.f ? av / kFp8Max : 1.0f;
+    float yk[8], yv[8];
+    auto in_range = [](float s) { return s >= 0x1p-80f && s <= 0x1p80f; };
+    if (in_range(sk) && in_range(sv)) {  // the same for the whole group
+      const float rk = 1.0f / sk, rv = 1.0f / sv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        yk[i] = div_by_scale(xk[i], sk, rk);
+        yv[i] = div_by_scale(xv[i], sv, rv);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        yk[i] = xk[i] / sk;
+        yv[i] = xv[i] / sv;
+      }
+    }
+    const int64_t dst = dst_row * 128 + 8 * sub;
+    __builtin_nontemporal_store(encode_fp8x8(yk), reinterpret_cast<u32x2*>((uint8_t*)k_pool + dst));
+    __builtin_nontemporal_store(encode_fp8x8(yv), reinterpret_cast<u32x2*>((uint8_t*)v_pool + dst));
+    if (sub == 0) {
+      k_scale[dst_row] = sk;
+      v_scale[dst_row] = sv;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const void* segs,
+                            const int32_t* seg_indptr, const int32_t* cu_new, const int32_t* cu_k,
+                            int batch, int total_new, int hkv, int64_t pool_tokens, int fp8,
+                            void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                            hipStream_t stream) {
+  const int64_t rows = (int64_t)total_new * hkv;
+  if (rows == 0) return hipSuccess;
+  if (rows > INT32_MAX) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  auto kern = fp8 ? kv_append_kernel<true> : kv_append_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, (const uint16_t*)k_new,
+                     (const uint16_t*)v_new, (const Seg*)segs, seg_indptr, cu_new, cu_k, batch,
+                     total_new, hkv, pool_tokens, k_pool, v_pool, k_scale, v_scale);
+  return hipGetLastError();
+}
+
+}  // namespace segattn

@@ -6,7 +6,9 @@ Q_len = K_len = 1024, 64 q / 8 kv heads, d = 128, bf16, KV in one segment of a 1
 pool). One step = one seg_attn_prefill call over that batch; the headline value is
 causal-adjusted TFLOPS (4 * d * Hq * visible (q, k) pairs per second). The other workloads
 (chunked prefill, bf16 decode, FP8 long decode) are measured in the same run and reported
-under "configs" (prefill: TFLOPS; decode: KV-read GB/s), unless --quick.
+under "configs" (prefill: TFLOPS; decode: KV-read GB/s), and the KV appends that precede the
+attention calls of those workloads under "append" (GB/s of rows read and written), unless
+--quick.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -27,7 +29,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = {"prefill": "attention_segmented_kv_amd/csrc/prefill.hip",
-                  "decode": "attention_segmented_kv_amd/csrc/decode.hip"}
+                  "decode": "attention_segmented_kv_amd/csrc/decode.hip",
+                  "append": "attention_segmented_kv_amd/csrc/append.hip"}
 
 
 def log(*a):
@@ -48,6 +51,66 @@ def decode_kv_bytes(w) -> float:
     if w.kv_dtype != "bf16":
         per_tok += w.num_heads_kv * 4 * 2  # one fp32 scale each for K and V
     return float(w.k_lens.sum()) * per_tok
+
+
+def append_bytes(n_rows: int, fp8: bool) -> float:
+    """Algorithmic HBM bytes of appending n_rows (token, kv head) rows of K and of V: the bf16
+    rows read (2 x 256 B), and either the bf16 rows written (2 x 256 B) or the FP8 codes and
+    scales written (2 x (128 + 4) B)."""
+    return float(n_rows) * (512 + (264 if fp8 else 512))
+
+
+# The appends measured beside attention: the writes one step of a workload makes before its
+# attention call (each request's last Lq_b keys are new), with its tables and pool size.
+APPEND_CASES = (("append_chunk_bf16_4x2048", 3, "bf16"), ("append_chunk_fp8_4x2048", 3, "fp8_e4m3"),
+                ("append_decode_bf16_b128", 4, "bf16"), ("append_decode_fp8_b16", 5, "fp8_e4m3"))
+
+
+APPEND_REPS = 10
+
+
+def measure_append(name, c, fmt, steps, warmup, dev):
+    import numpy as np
+    import torch
+    import attention_segmented_kv_amd as sa
+    import workloads as wl
+    w = wl.make_config(c, device=dev, poison=False)
+    n_new = w.q_lens.astype(np.int64)
+    cu_new = torch.as_tensor(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).to(dev)
+    total = int(n_new.sum())
+    g = torch.Generator(device=dev)
+    g.manual_seed(7000 + c)
+    shape = (total, w.num_heads_kv, w.head_dim)
+    k_new = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    v_new = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    fp8 = fmt == "fp8_e4m3"
+    if fp8 == (w.kv_dtype == "fp8_e4m3"):
+        kp, vp, ks, vs = w.k_pool, w.v_pool, w.k_scale, w.v_scale
+    else:  # same tables, the other pool format (the append never reads the pool)
+        pshape = tuple(w.k_pool.shape)
+        kp = torch.zeros(pshape, dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn)
+        vp = torch.zeros(pshape, dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn)
+        ks = torch.ones(pshape[:2], dtype=torch.float32, device=dev)
+        vs = torch.ones(pshape[:2], dtype=torch.float32, device=dev)
+
+    # An append is a few microseconds of GPU work, less than the binding's host time per call,
+    # so the timed unit is a HIP graph of APPEND_REPS appends, replayed; per-append figures are
+    # per replay / APPEND_REPS.
+    def step():
+        for _ in range(APPEND_REPS):
+            sa.kv_append(k_new, v_new, w.segs, w.seg_indptr, cu_new, w.cu_seqlens_k, kp, vp,
+                         k_scale=ks, v_scale=vs)
+    t = time_steps(step, steps, warmup, graph=True)
+    t["launch_ms_mean"] /= APPEND_REPS
+    t["ms_per_step"] /= APPEND_REPS
+    work = append_bytes(total * w.num_heads_kv, fp8)
+    achieved = work / (t["launch_ms_mean"] * 1e-3) / 1e9
+    rf = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+          "frac": achieved / PEAK_HBM_GBS, "traffic": load_traffic("append", name)}
+    return {"workload": name, "tables_of": w.name, "new_tokens": total, "kv": fmt,
+            "value": round(work / (t["ms_per_step"] * 1e-3) / 1e9, 3), "unit": "GB/s",
+            "launch_us_mean": round(t["launch_ms_mean"] * 1e3, 2), "roofline": rf,
+            "work_per_step": work, "timing": "graph replays of %d appends" % APPEND_REPS}
 
 
 def make_step(w):
@@ -181,6 +244,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph capturing one step instead of eager calls")
+    ap.add_argument("--append-only", default=None, metavar="NAME|all",
+                    help="only time the KV appends (one named case, or all), one line each on stderr")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB, 5 times (reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -206,6 +271,20 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 5}}))
+        return
+
+    if args.append_only:
+        res = []
+        for name, c, fmt in APPEND_CASES:
+            if args.append_only not in ("all", name):
+                continue
+            log(f"[bench] timing {name}: warmup {args.warmup}, steps {args.steps}")
+            r = measure_append(name, c, fmt, args.steps, args.warmup, dev)
+            log(f"[bench] {name}: {r['value']:.1f} GB/s per step, launch mean {r['launch_us_mean']:.2f} us, "
+                f"roofline frac {r['roofline']['frac']:.3f}")
+            res.append(r)
+            torch.cuda.empty_cache()
+        print(json.dumps({"append": res}), flush=True)
         return
 
     head_c = args.config
@@ -255,6 +334,15 @@ def main():
             del wc
             torch.cuda.empty_cache()
         result["configs"] = extra
+        app = []
+        for name, c, fmt in APPEND_CASES:
+            log(f"[bench] {name}: generating")
+            r = measure_append(name, c, fmt, max(20, args.steps // 2), args.warmup, dev)
+            log(f"[bench] {name}: {r['value']:.1f} GB/s, launch mean {r['launch_us_mean']:.2f} us, "
+                f"frac {r['roofline']['frac']:.3f}")
+            app.append(r)
+            torch.cuda.empty_cache()
+        result["append"] = app
 
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

@@ -11,7 +11,8 @@
  * not) and a single-token decode that splits each request's keys into blocks, computes partial
  * results per block and reduces them per request with a log-sum-exp merge (FlashAccel article,
  * "data layout": blockwise partial attention reduced per request; the running max m_i and
- * normaliser l_i of "FlashAttention on Ascend NPU", bottleneck 2).
+ * normaliser l_i of "FlashAttention on Ascend NPU", bottleneck 2). A third writes new tokens
+ * into the segments (bf16, or FP8 quantised on write) ahead of either.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -40,7 +41,8 @@
  * Causal:     aligned bottom-right: query i of request b sits at key position K_b - Lq_b + i
  *             and sees keys 0 .. K_b - Lq_b + i (this is what chunked prefill needs).
  * Supported:  head_dim == 128 and Hq / Hkv == 8 (64 q / 8 kv heads, or any Hkv with 8 query
- *             heads per kv head); other shapes return SEG_ATTN_ERR_UNSUPPORTED.
+ *             heads per kv head; the append needs only head_dim == 128); other shapes return
+ *             SEG_ATTN_ERR_UNSUPPORTED.
  */
 #ifndef SEG_ATTN_H_
 #define SEG_ATTN_H_
@@ -137,6 +139,46 @@ size_t seg_attn_decode_workspace_bytes(int32_t batch, int32_t max_seqlen_k, int3
  * num_splits > 0, the smallest length the device may pick for 0. Returns -1 on invalid sizes. */
 int32_t seg_attn_decode_num_splits(int32_t batch, int32_t max_seqlen_k, int32_t num_heads_kv,
                                    int32_t kv_dtype, int32_t num_splits, int32_t* split_len);
+
+/*
+ * KV append: write a batch's new tokens' K and V rows into the pool slots their requests'
+ * segments give them, the step that precedes attention on every prefill chunk and decode token.
+ * The pages imply it without describing it: each request's cache is a few contiguous segments
+ * of one shared pool (Flood README, "Introduction"), and an FP8 KV cache is among the same
+ * README's features; the FP8 row format is the one seg_attn_decode reads.
+ *
+ * k_new/v_new  [total_new, Hkv, 128] bf16, the new tokens of all requests in request order.
+ * segs, seg_indptr: the tables AFTER the caller has grown each request's segments to hold its
+ *              new tokens (device).
+ * cu_seqlens_new [batch+1] int32 (device): request b appends
+ *              n_b = cu_seqlens_new[b+1] - cu_seqlens_new[b] tokens, rows
+ *              cu_seqlens_new[b] .. cu_seqlens_new[b+1]-1 of k_new/v_new.
+ * cu_seqlens_k [batch+1] int32 (device): key counts K_b AFTER the append. Request b's new
+ *              tokens become its last n_b keys, logical positions K_b - n_b .. K_b - 1, in row
+ *              order; n_b <= K_b and the segment lengths of b must sum to K_b.
+ * total_new    HOST, must equal cu_seqlens_new[batch]; it sizes the launch.
+ * kv_dtype     SEG_ATTN_KV_BF16: rows are copied bit for bit. SEG_ATTN_KV_FP8_E4M3: per
+ *              (token, kv head) row x the scale s = max|x| / 448 in fp32 (1 for an all-zero row)
+ *              goes to k_scale/v_scale[slot, head] and the codes E4M3FN(clamp(x / s, +-448)),
+ *              x / s an fp32 division and the conversion rounding to nearest, ties to even, go
+ *              to the pool; the largest |x| of a row is stored as +-448.
+ * k_pool/v_pool[pool_tokens, Hkv, 128] bf16 or E4M3FN bytes; k_scale/v_scale [pool_tokens, Hkv]
+ *              fp32 for FP8 (required), ignored for bf16. Only the new tokens' slots (and their
+ *              scales) are written; every other slot is left as it was.
+ * k_new, v_new and bf16 pools must be 16-byte aligned, FP8 pools 8-byte, scales 4-byte
+ * (SEG_ATTN_ERR_INVALID_ARG otherwise); torch and hipMalloc allocations are.
+ * A key whose slot falls outside the request's segments or the pool is skipped, never written
+ * out of bounds; this only happens with tables that break the rules above. New tokens of
+ * different requests must not share a slot (the writes would race).
+ * Returns SEG_ATTN_OK, or an error before anything is launched.
+ */
+seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
+                                     const seg_attn_segment_t* segs, const int32_t* seg_indptr,
+                                     const int32_t* cu_seqlens_new, const int32_t* cu_seqlens_k,
+                                     int32_t batch, int32_t total_new, int32_t num_heads_kv,
+                                     int32_t head_dim, int64_t pool_tokens, int32_t kv_dtype,
+                                     void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                     seg_attn_stream_t stream);
 
 /* Static text for a status code; never NULL. */
 const char* seg_attn_status_string(seg_attn_status_t status);

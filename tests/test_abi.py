@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    for s in ("seg_attn_prefill", "seg_attn_decode", "seg_attn_decode_workspace_bytes",
+    for s in ("seg_attn_prefill", "seg_attn_decode", "seg_attn_kv_append", "seg_attn_decode_workspace_bytes",
               "seg_attn_decode_num_splits", "seg_attn_status_string", "seg_attn_validate_tables",
               "seg_attn_version"):
         assert s in syms
@@ -88,6 +88,34 @@ def _decode_args(**over):
 def test_decode_rejects_bad_arguments(over, status):
     lib = _lib()
     assert lib.seg_attn_decode(*_decode_args(**over)) == status
+
+
+def _append_args(**over):
+    # nonzero, suitably aligned stand-ins for device pointers: every case is rejected (or is a
+    # no-op) before anything is launched
+    a = dict(kn=256, vn=256, segs=1, ind=1, cn=1, ck=1, batch=2, tn=5, hkv=8, d=128, pool=16, kvd=0,
+             kp=256, vp=256, ks=None, vs=None, stream=None)
+    a.update(over)
+    return [a[k] for k in ("kn", "vn", "segs", "ind", "cn", "ck", "batch", "tn", "hkv", "d", "pool", "kvd",
+                           "kp", "vp", "ks", "vs", "stream")]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kn=None), 1), (dict(vp=None), 1), (dict(cn=None), 1), (dict(batch=-1), 1), (dict(tn=-2), 1),
+    (dict(hkv=0), 1), (dict(pool=-1), 1), (dict(kvd=3), 1), (dict(kvd=1), 1), (dict(kvd=1, ks=1), 1),
+    (dict(d=64), 2), (dict(pool=2 ** 31), 2), (dict(batch=0), 1),
+    (dict(kn=16 + 8), 1), (dict(kp=2), 1), (dict(kvd=1, ks=4, vs=6, kp=8, vp=16), 1),
+    (dict(vn=264), 1),
+])
+def test_kv_append_rejects_bad_arguments(over, status):
+    lib = _lib()
+    assert lib.seg_attn_kv_append(*_append_args(**over)) == status
+
+
+def test_kv_append_without_new_tokens_is_a_noop():
+    lib = _lib()
+    assert lib.seg_attn_kv_append(*_append_args(tn=0, kn=None, vn=None, kp=None, vp=None)) == 0
+    assert lib.seg_attn_kv_append(*_append_args(batch=0, tn=0)) == 0
 
 
 def test_split_plan_and_workspace_size():
