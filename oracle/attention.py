@@ -27,7 +27,9 @@ notes):
     listed Flood feature, needs exactly this; decode then sees every key);
   * a request's logical key order is the order of its segments in the table;
   * pool layout is token-major [pool_tokens, Hkv, D]; FP8 pools are OCP E4M3FN codes times
-    one fp32 scale per (token, kv head);
+    one fp32 scale per (token, kv head), INT8 pools two's-complement int8 codes times one fp32
+    scale per (token, kv head) (the INT8 KV cache of "FlashAttention on Ascend NPU",
+    optimisation 3, with the FP8 cache's per-row scale);
   * a query row with no visible key returns O = 0 and LSE = -inf.
 """
 from __future__ import annotations
@@ -65,13 +67,20 @@ def e4m3fn_to_f64(bits: np.ndarray) -> np.ndarray:
     return out
 
 
+def int8_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Bytes read as two's-complement 8-bit integers (0x80..0xFF are -128..-1)."""
+    return np.asarray(bits).astype(np.uint8).view(np.int8).astype(np.float64)
+
+
 def decode_kv(bits: np.ndarray, scale: Optional[np.ndarray], fmt: str) -> np.ndarray:
-    """Decoded K or V rows [n, Hkv, D] in float64. For FP8 the code is multiplied by its
-    per-(token, kv head) fp32 scale; the product of two such numbers is exact in float64."""
+    """Decoded K or V rows [n, Hkv, D] in float64. For FP8 and INT8 the code is multiplied by
+    its per-(token, kv head) fp32 scale; the product of two such numbers is exact in float64."""
     if fmt == "bf16":
         return bf16_to_f64(bits)
     if fmt == "fp8_e4m3":
         return e4m3fn_to_f64(bits) * np.asarray(scale, dtype=np.float64)[..., None]
+    if fmt == "int8":
+        return int8_to_f64(bits) * np.asarray(scale, dtype=np.float64)[..., None]
     raise ValueError(f"unknown kv format {fmt}")
 
 

@@ -15,7 +15,12 @@ same README lists an FP8 KV cache among its features). Readings taken here:
 - an FP8 pool stores, per (token, kv head) row x of D bf16 values, one fp32 scale
   s = fp32(max|x| / 448) (s = 1 for an all-zero row) and the codes e4m3fn(clamp(x / s, ±448)),
   x / s computed as an fp32 division and the conversion rounding to nearest, ties to even
-  (OCP E4M3FN: bias 7, largest finite 448).
+  (OCP E4M3FN: bias 7, largest finite 448);
+- an INT8 pool (the INT8 KV cache of "FlashAttention on Ascend NPU", optimisation 3, which the
+  page leaves at "quantise to INT8") stores per row the symmetric scale s = fp32(max|x| / 127)
+  (1 for an all-zero row) and the codes round(clamp(x / s, ±127)) as two's-complement bytes,
+  x / s again an fp32 division and the rounding to nearest, ties to even; -128 is never
+  produced.
 """
 from typing import Optional
 
@@ -24,6 +29,7 @@ import numpy as np
 from .attention import request_slots
 
 FP8_MAX = 448.0
+INT8_MAX = 127.0
 
 
 def bf16_bits_to_f32(bits) -> np.ndarray:
@@ -68,14 +74,25 @@ def quantize_rows(x_f32: np.ndarray):
     return f32_to_e4m3fn(y), scale
 
 
+def quantize_rows_int8(x_f32: np.ndarray):
+    """Per-row INT8 encoding of float32 rows [..., D]: (codes as uint8 bytes [..., D], scales
+    float32 [...]). The quotient is rounded to an integer with np.rint (ties to even)."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(INT8_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[..., None]).astype(np.float32)
+    y = np.clip(y, np.float32(-INT8_MAX), np.float32(INT8_MAX))
+    return np.rint(y).astype(np.int8).view(np.uint8), scale
+
+
 def kv_append(k_new_bits, v_new_bits, segs, seg_indptr, cu_new, cu_k, k_pool, v_pool,
               k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None,
               fmt: str = "bf16"):
     """The pools after appending: copies of (k_pool, v_pool, k_scale, v_scale).
 
     k_new_bits / v_new_bits [T, Hkv, D] bf16 bit patterns (uint16), T = cu_new[B]; pools
-    [pool_tokens, Hkv, D] uint16 (bf16) or uint8 (fp8 codes); scales [pool_tokens, Hkv] fp32
-    for fp8."""
+    [pool_tokens, Hkv, D] uint16 (bf16) or uint8 (fp8 codes, int8 codes as bytes); scales
+    [pool_tokens, Hkv] fp32 for fp8 and int8."""
     kp, vp = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
     ks = None if k_scale is None else np.array(k_scale, dtype=np.float32, copy=True)
     vs = None if v_scale is None else np.array(v_scale, dtype=np.float32, copy=True)
@@ -94,9 +111,10 @@ def kv_append(k_new_bits, v_new_bits, segs, seg_indptr, cu_new, cu_k, k_pool, v_
         if fmt == "bf16":
             kp[dst] = np.asarray(k_new_bits)[src]
             vp[dst] = np.asarray(v_new_bits)[src]
-        elif fmt == "fp8_e4m3":
-            kc, kscale = quantize_rows(bf16_bits_to_f32(np.asarray(k_new_bits)[src]))
-            vc, vscale = quantize_rows(bf16_bits_to_f32(np.asarray(v_new_bits)[src]))
+        elif fmt in ("fp8_e4m3", "int8"):
+            quant = quantize_rows if fmt == "fp8_e4m3" else quantize_rows_int8
+            kc, kscale = quant(bf16_bits_to_f32(np.asarray(k_new_bits)[src]))
+            vc, vscale = quant(bf16_bits_to_f32(np.asarray(v_new_bits)[src]))
             kp[dst], ks[dst] = kc, kscale
             vp[dst], vs[dst] = vc, vscale
         else:

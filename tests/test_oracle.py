@@ -1,7 +1,7 @@
 """Pins for the CPU oracle: each test checks it against something other than itself.
 
-* number formats: the oracle's bf16 and E4M3FN decoders against torch's own conversions for
-  every code, plus points fixed by the OCP FP8 definition;
+* number formats: the oracle's bf16, E4M3FN and INT8 decoders against torch's own conversions
+  for every code, plus points fixed by the OCP FP8 definition;
 * brute force: an independent pure-Python evaluation (per-key segment lookup, absolute
   positions, math.exp / math.fsum) on tiny inputs;
 * a library routine: torch's scaled_dot_product_attention in float64 with an explicit mask;
@@ -62,6 +62,14 @@ def test_e4m3fn_decoder_matches_torch_for_every_code():
     assert np.array_equal(ours[ok], ref[ok])
 
 
+def test_int8_decoder_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    ours = oracle.int8_to_f64(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.int8).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+    assert ours[0x7F] == 127 and ours[0x80] == -128 and ours[0xFF] == -1
+
+
 def test_e4m3fn_fixed_points_of_the_format():
     # OCP 8-bit FP, E4M3: bias 7, max normal S.1111.110 = 448, min normal 2^-6,
     # min subnormal 2^-9, 1.0 = 0.0111.000, NaN = S.1111.111, negative zero 0x80.
@@ -81,7 +89,7 @@ def _brute(w):
     query positions for the causal test, scalar math.exp and math.fsum."""
     segs, ind, cq, ck = wl.host_tables(w)
     qf = w.q.to(torch.float64).numpy()
-    if w.kv_dtype == "fp8_e4m3":
+    if w.kv_dtype in ("fp8_e4m3", "int8"):
         kf = w.k_pool.to(torch.float64).numpy() * w.k_scale.to(torch.float64).numpy()[..., None]
         vf = w.v_pool.to(torch.float64).numpy() * w.v_scale.to(torch.float64).numpy()[..., None]
     else:
@@ -146,6 +154,14 @@ def test_oracle_equals_brute_force_fp8():
     assert np.abs(l - lb).max() < 1e-12
 
 
+def test_oracle_equals_brute_force_int8():
+    w = _tiny(12, batch=3, hq=4, hkv=2, d=8, kv_dtype="int8", zero_len=True)
+    o, l = _run_oracle(w)
+    ob, lb = _brute(w)
+    assert np.abs(o - ob).max() < 1e-12
+    assert np.abs(l - lb).max() < 1e-12
+
+
 def test_oracle_equals_brute_force_full_head_dim():
     w = _tiny(21, batch=1, hq=8, hkv=1, d=128, max_k=6)
     o, l = _run_oracle(w)
@@ -159,7 +175,7 @@ def test_oracle_equals_brute_force_full_head_dim():
 def _sdpa(w):
     segs, ind, cq, ck = wl.host_tables(w)
     q = w.q.to(torch.float64)
-    if w.kv_dtype == "fp8_e4m3":
+    if w.kv_dtype in ("fp8_e4m3", "int8"):
         kp = w.k_pool.to(torch.float64) * w.k_scale.to(torch.float64)[..., None]
         vp = w.v_pool.to(torch.float64) * w.v_scale.to(torch.float64)[..., None]
     else:
@@ -188,6 +204,13 @@ def test_oracle_equals_torch_sdpa(seed):
     w = wl.make_random(100 + seed, batch=3, q_lens=[5, 1, 17], k_lens=[9, 30, 40], max_segs=5,
                        num_heads_q=8, num_heads_kv=2, head_dim=32,
                        kv_dtype="fp8_e4m3" if seed == 3 else "bf16")
+    o, _ = _run_oracle(w)
+    assert np.abs(o - _sdpa(w)).max() < 1e-12
+
+
+def test_oracle_equals_torch_sdpa_int8():
+    w = wl.make_random(104, batch=3, q_lens=[4, 1, 9], k_lens=[12, 33, 20], max_segs=4,
+                       num_heads_q=8, num_heads_kv=2, head_dim=32, kv_dtype="int8")
     o, _ = _run_oracle(w)
     assert np.abs(o - _sdpa(w)).max() < 1e-12
 

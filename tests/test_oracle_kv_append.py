@@ -1,6 +1,7 @@
 """Pins of the KV-append oracle (CPU): the E4M3FN encoder against torch's float8 conversion,
-every code and hand-worked ties; the row quantiser's scale and extremes; the append against
-what it must leave in the pool, read back through the segment tables."""
+every code and hand-worked ties; the FP8 and INT8 row quantisers' scales, extremes and ties
+(INT8 also against torch's division and rounding); the append against what it must leave in
+the pool, read back through the segment tables."""
 import numpy as np
 import pytest
 import torch
@@ -77,7 +78,53 @@ def test_quantize_rows_scale_extremes_and_zero_rows():
     assert np.all(np.abs(dec - x) <= scale[..., None].astype(np.float64) * 16.0 * (1 + 1e-6))
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3"])
+def _torch_int8_rows(x: np.ndarray):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    amax = t.abs().amax(dim=-1)
+    sc = torch.where(amax > 0, amax / torch.tensor(127.0), torch.ones_like(amax))
+    q = torch.round((t / sc.unsqueeze(-1)).clamp(-127.0, 127.0)).to(torch.int8)
+    return q.view(torch.uint8).numpy(), sc.numpy()
+
+
+def test_int8_quantiser_matches_torch():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal((300, 8, 128)),
+                        rng.standard_normal((40, 8, 128)) * 1e-30,
+                        rng.uniform(-1e4, 1e4, (40, 8, 128))]).astype(np.float32)
+    x = oracle.bf16_bits_to_f32((x.view(np.uint32) >> 16).astype(np.uint16))  # bf16 values
+    codes, scale = oracle.quantize_rows_int8(x)
+    tc, ts = _torch_int8_rows(x)
+    assert np.array_equal(scale, ts) and np.array_equal(codes, tc)
+
+
+def test_int8_quantiser_ties_extremes_and_zero_rows():
+    # a row whose largest magnitude is 127 has scale exactly 1, so x / s = x: the hand-worked
+    # ties 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, 3.5 -> 4, -2.5 -> -2, -0.5 -> 0, 126.5 -> 126
+    row = np.zeros(128, dtype=np.float32)
+    vals = [0.5, 1.5, 2.5, 3.5, -2.5, -0.5, 126.5, 127.0, -127.0, 5.0]
+    row[:len(vals)] = vals
+    codes, scale = oracle.quantize_rows_int8(row[None])
+    assert scale[0] == 1.0
+    got = codes[0, :len(vals)].view(np.int8).tolist()
+    assert got == [0, 2, 2, 4, -2, 0, 126, 127, -127, 5]
+    # zero row: scale 1, all codes 0; the extreme element of any other row is +-127; the error
+    # is at most half a step (exact ties reach it) plus the quotient's fp32 rounding
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((50, 8, 128)).astype(np.float32)
+    x[7, 2] = 0.0
+    codes, scale = oracle.quantize_rows_int8(x)
+    assert scale[7, 2] == 1.0 and not codes[7, 2].any()
+    c = codes.view(np.int8).astype(np.int64)
+    idx = np.abs(x).argmax(axis=-1)
+    top = np.take_along_axis(c, idx[..., None], axis=-1)[..., 0]
+    nz = np.abs(x).max(axis=-1) > 0
+    assert np.all(np.abs(top[nz]) == 127) and c.min() >= -127
+    dec = c * scale[..., None].astype(np.float64)
+    # half a step, plus the fp32 rounding of the quotient (at most 127 * 2^-24 steps)
+    assert np.all(np.abs(dec - x) <= scale[..., None].astype(np.float64) * (0.5 + 2.0 ** -16))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3", "int8"])
 def test_kv_append_writes_the_last_keys_and_nothing_else(fmt):
     gen = torch.Generator().manual_seed(3)
     # four requests with segments (one with none), new tokens at the end of each
@@ -101,6 +148,14 @@ def test_kv_append_writes_the_last_keys_and_nothing_else(fmt):
         src = slice(int(cu_new[b]), int(cu_new[b + 1]))
         if fmt == "bf16":
             assert np.array_equal(kp[slots], k_new[src]) and np.array_equal(vp[slots], v_new[src])
+        elif fmt == "int8":
+            for pool, sc, new in ((kp, ks, k_new), (vp, vs, v_new)):
+                x = oracle.bf16_to_f64(new[src])
+                amax = np.abs(x).max(axis=-1)
+                assert np.array_equal(sc[slots], np.where(amax > 0, amax.astype(np.float32) / np.float32(127), 1))
+                dec = oracle.int8_to_f64(pool[slots]) * sc[slots][..., None]
+                # half a step, plus the fp32 rounding of the quotient (at most 127 * 2^-24 steps)
+                assert np.all(np.abs(dec - x) <= sc[slots][..., None].astype(np.float64) * (0.5 + 2.0 ** -16))
         else:
             for pool, sc, new in ((kp, ks, k_new), (vp, vs, v_new)):
                 x = oracle.bf16_to_f64(new[src])

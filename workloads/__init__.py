@@ -9,20 +9,22 @@ attention.
 
 Layouts (the same ones the C-ABI takes):
   q            [total_q, Hq, D]        bfloat16
-  k_pool/v_pool[pool_tokens, Hkv, D]   bfloat16 or float8_e4m3fn
-  k_scale/v_scale [pool_tokens, Hkv]   float32 (FP8 pool only)
+  k_pool/v_pool[pool_tokens, Hkv, D]   bfloat16, float8_e4m3fn or int8
+  k_scale/v_scale [pool_tokens, Hkv]   float32 (FP8 and INT8 pools only)
   segs         [nseg, 2] int32 rows of (pool_offset, length), grouped by request
                in logical key order
   seg_indptr   [B + 1] int32, request b owns segs[seg_indptr[b]:seg_indptr[b+1]]
   cu_seqlens_q, cu_seqlens_k  [B + 1] int32 prefix sums of query / key lengths
 
-Pool slots no segment references are filled with NaN when ``poison`` is set,
-so that any read outside the segments shows up in the output.
+Pool slots no segment references are filled with NaN when ``poison`` is set
+(INT8 pools: code -128 with a NaN scale), so that any read outside the segments
+shows up in the output.
 
 The five named configurations follow the workload shapes of the Flood README
 ("Kernels / Seg-attn" table: 64 query heads, 8 kv heads, head dim 128, batch 1
 with Q_len = K_len = 1024, batch 128 with Q_len = 1) plus chunked prefill and a
-long FP8 decode; the exact recipe for each is in ``CONFIGS``.
+long FP8 decode; a sixth is the long decode over an INT8 pool. The exact recipe
+for each is in ``CONFIGS``.
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ import torch
 
 HQ, HKV, HEAD_DIM = 64, 8, 128
 FP8_MAX = 448.0  # largest finite OCP E4M3FN value
+INT8_MAX = 127.0  # largest INT8 code the symmetric encoding uses
 
 
 @dataclass
@@ -173,6 +176,17 @@ def encode_fp8_rows(x: torch.Tensor):
     return codes, scale
 
 
+def encode_int8_rows(x: torch.Tensor):
+    """Input encoding of an N(0,1) fp32 block [..., D] as symmetric INT8 codes plus one fp32
+    scale per row: scale = max|x| / 127, code = round-half-even(clamp(x / scale, +-127)), with
+    torch's own division and rounding. Like ``encode_fp8_rows`` it only prepares the input
+    pool."""
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / INT8_MAX, torch.ones_like(amax)).to(torch.float32)
+    codes = torch.round((x / scale.unsqueeze(-1)).clamp(-INT8_MAX, INT8_MAX)).to(torch.int8)
+    return codes, scale
+
+
 def build(name: str, kind: str, q_lens: Sequence[int], seg_lengths: Sequence[Sequence[int]],
           pool_tokens: int, *, seed: int, rng: np.random.Generator, causal: bool,
           kv_dtype: str = "bf16", num_heads_q: int = HQ, num_heads_kv: int = HKV,
@@ -202,17 +216,24 @@ def build(name: str, kind: str, q_lens: Sequence[int], seg_lengths: Sequence[Seq
     total_q = int(cu_q[-1])
     q = torch.randn((total_q, num_heads_q, head_dim), generator=gen, device=device,
                     dtype=torch.float32).to(torch.bfloat16)
+    if kv_dtype not in ("bf16", "fp8_e4m3", "int8"):
+        raise ValueError(f"unknown kv dtype {kv_dtype}")
     fp8 = kv_dtype == "fp8_e4m3"
-    pool_dtype = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    int8 = kv_dtype == "int8"
+    scaled = fp8 or int8
+    pool_dtype = torch.float8_e4m3fn if fp8 else (torch.int8 if int8 else torch.bfloat16)
     shape = (pool_tokens, num_heads_kv, head_dim)
-    if poison:
+    if poison and int8:
+        k_pool = torch.full(shape, -128, dtype=torch.int8, device=device)
+        v_pool = torch.full(shape, -128, dtype=torch.int8, device=device)
+    elif poison:
         k_pool = _nan_tensor(shape, pool_dtype, device)
         v_pool = _nan_tensor(shape, pool_dtype, device)
     else:
         k_pool = torch.zeros(shape, dtype=pool_dtype, device=device)
         v_pool = torch.zeros(shape, dtype=pool_dtype, device=device)
     k_scale = v_scale = None
-    if fp8:
+    if scaled:
         fill = float("nan") if poison else 1.0
         k_scale = torch.full((pool_tokens, num_heads_kv), fill, dtype=torch.float32, device=device)
         v_scale = torch.full((pool_tokens, num_heads_kv), fill, dtype=torch.float32, device=device)
@@ -221,9 +242,10 @@ def build(name: str, kind: str, q_lens: Sequence[int], seg_lengths: Sequence[Seq
         kb = int(k_lens[b])
         kx = torch.randn((kb, num_heads_kv, head_dim), generator=gen, device=device, dtype=torch.float32)
         vx = torch.randn((kb, num_heads_kv, head_dim), generator=gen, device=device, dtype=torch.float32)
-        if fp8:
-            kc, ks = encode_fp8_rows(kx)
-            vc, vs = encode_fp8_rows(vx)
+        if scaled:
+            enc = encode_fp8_rows if fp8 else encode_int8_rows
+            kc, ks = enc(kx)
+            vc, vs = enc(vx)
         else:
             kc, vc = kx.to(torch.bfloat16), vx.to(torch.bfloat16)
         start = 0
@@ -232,7 +254,7 @@ def build(name: str, kind: str, q_lens: Sequence[int], seg_lengths: Sequence[Seq
             if ln:
                 k_pool[off:off + ln] = kc[start:start + ln]
                 v_pool[off:off + ln] = vc[start:start + ln]
-                if fp8:
+                if scaled:
                     k_scale[off:off + ln] = ks[start:start + ln]
                     v_scale[off:off + ln] = vs[start:start + ln]
             start += ln
@@ -249,7 +271,7 @@ def build(name: str, kind: str, q_lens: Sequence[int], seg_lengths: Sequence[Seq
 
 
 # ----------------------------------------------------------------------------------------------
-# the five named configurations
+# the named configurations
 
 CONFIGS = {
     1: "tiny causal prefill: B=1, Lq=K=128, 64/8/128 bf16 N(0,1), KV as 2 segments (80 + 48) at "
@@ -262,14 +284,17 @@ CONFIGS = {
        "per request, 2^20-slot pool, 64/8/128 bf16",
     5: "FP8 long decode: B=16, Lq=1, K ~ U{32768..131072}, 1-8 segments per request, 2^21-slot "
        "pool, Q bf16, K/V e4m3fn + fp32 scale per (token, kv head), 64/8/128",
+    6: "INT8 long decode: the FP8 long decode's shape and recipe with K/V as symmetric int8 codes "
+       "+ fp32 scale per (token, kv head)",
 }
 
 CONFIG_NAMES = {1: "tiny_prefill_128", 2: "prefill_1k", 3: "chunked_prefill_4x2048",
-                4: "decode_bf16_b128_lognormal", 5: "decode_fp8_b16_32k_128k"}
+                4: "decode_bf16_b128_lognormal", 5: "decode_fp8_b16_32k_128k",
+                6: "decode_int8_b16_32k_128k"}
 
 
 def make_config(c: int, *, seed: Optional[int] = None, device="cpu", poison: bool = True) -> Workload:
-    """One of the five named configurations, seeded with 1000 + c unless ``seed`` is given."""
+    """One of the named configurations (1..6), seeded with 1000 + c unless ``seed`` is given."""
     s = 1000 + c if seed is None else seed
     rng = np.random.default_rng(s)
     name, recipe = CONFIG_NAMES[c], CONFIGS[c]
@@ -295,13 +320,14 @@ def make_config(c: int, *, seed: Optional[int] = None, device="cpu", poison: boo
         segl = [cut_lengths(rng, int(k), int(n)) for k, n in zip(ks, nseg)]
         return build(name, "decode", [1] * B, segl, 1 << 20, seed=s, rng=rng, causal=True,
                      device=device, poison=poison, recipe=recipe)
-    if c == 5:
+    if c in (5, 6):
         B = 16
         ks = rng.integers(32768, 131072 + 1, size=B)
         nseg = rng.integers(1, 8 + 1, size=B)
         segl = [cut_lengths(rng, int(k), int(n)) for k, n in zip(ks, nseg)]
         return build(name, "decode", [1] * B, segl, 1 << 21, seed=s, rng=rng, causal=True,
-                     kv_dtype="fp8_e4m3", device=device, poison=poison, recipe=recipe)
+                     kv_dtype="fp8_e4m3" if c == 5 else "int8", device=device, poison=poison,
+                     recipe=recipe)
     raise ValueError(f"unknown config {c}")
 
 
@@ -334,11 +360,11 @@ def make_random(seed: int, *, batch: int, q_lens: Sequence[int], k_lens: Sequenc
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """Raw storage bits of a bf16 (uint16) or fp8 (uint8) tensor as a host numpy array."""
+    """Raw storage bits of a bf16 (uint16), fp8 or int8 (uint8) tensor as a host numpy array."""
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.int8):
         return t.view(torch.uint8).numpy()
     raise TypeError(f"no bit view for {t.dtype}")
 
