@@ -21,10 +21,13 @@ from typing import Optional
 import torch
 
 __all__ = ["prefill", "decode", "kv_append", "decode_num_splits", "decode_workspace_bytes", "validate_tables",
-           "status_string", "version", "library_path", "SegAttnError", "KV_BF16", "KV_FP8_E4M3"]
+           "status_string", "version", "library_path", "SegAttnError", "KV_BF16", "KV_FP8_E4M3",
+           "KV_INT8"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
+KV_INT8 = 2
+_KV_OF_DTYPE = {torch.bfloat16: KV_BF16, torch.float8_e4m3fn: KV_FP8_E4M3, torch.int8: KV_INT8}
 HEAD_DIM = 128
 GROUP = 8
 
@@ -186,31 +189,33 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: to
            workspace: Optional[torch.Tensor] = None, return_lse: bool = False):
     """Single-token decode with split-K and a log-sum-exp merge; see seg_attn_decode.
 
-    q [B, Hq, 128] bf16; k_pool/v_pool [pool_tokens, Hkv, 128] bf16, or float8_e4m3fn with
-    k_scale/v_scale [pool_tokens, Hkv] fp32. A workspace is allocated here unless given."""
+    q [B, Hq, 128] bf16; k_pool/v_pool [pool_tokens, Hkv, 128] bf16, or float8_e4m3fn / int8
+    codes with k_scale/v_scale [pool_tokens, Hkv] fp32. A workspace is allocated here unless
+    given."""
     lib = _load()
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("q must be a GPU tensor")
     _check(q, "q", (torch.bfloat16,), dev, 3)
-    fp8 = k_pool.dtype == torch.float8_e4m3fn
-    kv_types = (torch.float8_e4m3fn,) if fp8 else (torch.bfloat16,)
-    _check(k_pool, "k_pool", kv_types, dev, 3)
-    _check(v_pool, "v_pool", kv_types, dev, 3)
+    if k_pool.dtype not in _KV_OF_DTYPE:
+        raise TypeError(f"k_pool has dtype {k_pool.dtype}: expected bfloat16, float8_e4m3fn or int8")
+    kv_dtype = _KV_OF_DTYPE[k_pool.dtype]
+    scaled = kv_dtype != KV_BF16
+    _check(k_pool, "k_pool", (k_pool.dtype,), dev, 3)
+    _check(v_pool, "v_pool", (k_pool.dtype,), dev, 3)
     if k_pool.shape != v_pool.shape:
         raise ValueError("k_pool and v_pool must have the same shape")
     batch, hq, d = q.shape
     pool_tokens, hkv, _ = k_pool.shape
     _check_tables(segs, seg_indptr, (cu_seqlens_k,), dev, batch + 1,
                   ("segs", "seg_indptr", "cu_seqlens_k"))
-    if fp8:
+    if scaled:
         if k_scale is None or v_scale is None:
-            raise ValueError("an fp8 pool needs k_scale and v_scale")
+            raise ValueError("an fp8 or int8 pool needs k_scale and v_scale")
         for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
             _check(t, nm, (torch.float32,), dev, 2)
             if tuple(t.shape) != (pool_tokens, hkv):
                 raise ValueError(f"{nm} must have shape [pool_tokens, Hkv]")
-    kv_dtype = KV_FP8_E4M3 if fp8 else KV_BF16
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -248,8 +253,8 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, segs: torch.Tensor, seg_
 
     k_new/v_new [total_new, Hkv, 128] bf16; segs/seg_indptr/cu_seqlens_k describe the requests
     after the append (their last n_b keys are the new tokens); cu_seqlens_new [B+1] int32.
-    A bf16 pool gets the rows as they are; a float8_e4m3fn pool gets per-row scaled codes and
-    k_scale/v_scale [pool_tokens, Hkv] fp32 the scales."""
+    A bf16 pool gets the rows as they are; a float8_e4m3fn or int8 pool gets per-row scaled
+    codes and k_scale/v_scale [pool_tokens, Hkv] fp32 the scales."""
     lib = _load()
     dev = k_new.device
     if dev.type != "cuda":
@@ -258,10 +263,12 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, segs: torch.Tensor, seg_
     _check(v_new, "v_new", (torch.bfloat16,), dev, 3)
     if k_new.shape != v_new.shape:
         raise ValueError("k_new and v_new must have the same shape")
-    fp8 = k_pool.dtype == torch.float8_e4m3fn
-    kv_types = (torch.float8_e4m3fn,) if fp8 else (torch.bfloat16,)
-    _check(k_pool, "k_pool", kv_types, dev, 3)
-    _check(v_pool, "v_pool", kv_types, dev, 3)
+    if k_pool.dtype not in _KV_OF_DTYPE:
+        raise TypeError(f"k_pool has dtype {k_pool.dtype}: expected bfloat16, float8_e4m3fn or int8")
+    kv_dtype = _KV_OF_DTYPE[k_pool.dtype]
+    scaled = kv_dtype != KV_BF16
+    _check(k_pool, "k_pool", (k_pool.dtype,), dev, 3)
+    _check(v_pool, "v_pool", (k_pool.dtype,), dev, 3)
     if k_pool.shape != v_pool.shape:
         raise ValueError("k_pool and v_pool must have the same shape")
     total_new, hkv, d = k_new.shape
@@ -271,9 +278,9 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, segs: torch.Tensor, seg_
     batch = cu_seqlens_new.shape[0] - 1
     _check_tables(segs, seg_indptr, (cu_seqlens_new, cu_seqlens_k), dev, batch + 1,
                   ("segs", "seg_indptr", "cu_seqlens_new", "cu_seqlens_k"))
-    if fp8:
+    if scaled:
         if k_scale is None or v_scale is None:
-            raise ValueError("an fp8 pool needs k_scale and v_scale")
+            raise ValueError("an fp8 or int8 pool needs k_scale and v_scale")
         for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
             _check(t, nm, (torch.float32,), dev, 2)
             if tuple(t.shape) != (pool_tokens, hkv):
@@ -282,9 +289,9 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, segs: torch.Tensor, seg_
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.seg_attn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(segs), _ptr(seg_indptr),
                                     _ptr(cu_seqlens_new), _ptr(cu_seqlens_k), batch, total_new, hkv, d,
-                                    pool_tokens, KV_FP8_E4M3 if fp8 else KV_BF16, _ptr(k_pool),
-                                    _ptr(v_pool), _ptr(k_scale if fp8 else None),
-                                    _ptr(v_scale if fp8 else None), stream)
+                                    pool_tokens, kv_dtype, _ptr(k_pool), _ptr(v_pool),
+                                    _ptr(k_scale if scaled else None),
+                                    _ptr(v_scale if scaled else None), stream)
     if st != 0:
         raise SegAttnError("seg_attn_kv_append", st)
 

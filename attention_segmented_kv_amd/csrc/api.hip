@@ -16,14 +16,14 @@ hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
                           int batch, int max_seqlen_q, int hkv, float scale, int causal, void* out,
                           float* lse, int cu_count, int force_tile, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
-                         const float* k_scale, const float* v_scale, int fp8, const void* segs,
+                         const float* k_scale, const float* v_scale, int kv, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,
                          int forced_len, int min_len, int max_chunks, int cu_count, float scale,
                          void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* recs,
                          float* ws_o, float* ws_lse, hipStream_t stream);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const void* segs,
                             const int32_t* seg_indptr, const int32_t* cu_new, const int32_t* cu_k,
-                            int batch, int total_new, int hkv, int64_t pool_tokens, int fp8,
+                            int batch, int total_new, int hkv, int64_t pool_tokens, int fmt,
                             void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                             hipStream_t stream);
 }  // namespace segattn
@@ -52,6 +52,10 @@ int current_cu_count() {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+bool valid_kv_dtype(int32_t kv) {
+  return kv == SEG_ATTN_KV_BF16 || kv == SEG_ATTN_KV_FP8_E4M3 || kv == SEG_ATTN_KV_INT8;
+}
+
 // Decode chunk plan. Each request's keys are cut into chunks of one length; a chunk times a kv
 // head is one work unit of the split pass. With num_splits > 0 the length is fixed here:
 // ceil(max_k / num_splits) rounded up to a multiple of 64, so no request has more than
@@ -64,9 +68,9 @@ struct DecodePlan {
   int64_t per_request;   // upper bound of the chunks of one request
 };
 
-bool plan_decode(int batch, int max_k, int fp8, int requested, DecodePlan* p) {
+bool plan_decode(int batch, int max_k, int one_byte, int requested, DecodePlan* p) {
   if (batch < 0 || max_k < 0 || requested < 0) return false;
-  const int min_chunk = fp8 ? 1024 : 512;
+  const int min_chunk = one_byte ? 1024 : 512;
   if (requested > 0) {
     const int64_t len = std::max<int64_t>(kChunkGranule, ceil_div(ceil_div(max_k, requested), kChunkGranule) * kChunkGranule);
     p->forced_len = (int)len;
@@ -164,10 +168,10 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
 int32_t seg_attn_decode_num_splits(int32_t batch, int32_t max_seqlen_k, int32_t num_heads_kv,
                                    int32_t kv_dtype, int32_t num_splits, int32_t* split_len) {
   try {
-    if (kv_dtype != SEG_ATTN_KV_BF16 && kv_dtype != SEG_ATTN_KV_FP8_E4M3) return -1;
+    if (!valid_kv_dtype(kv_dtype)) return -1;
     if (num_heads_kv <= 0) return -1;
     DecodePlan p;
-    if (!plan_decode(batch, max_seqlen_k, kv_dtype == SEG_ATTN_KV_FP8_E4M3, num_splits, &p)) return -1;
+    if (!plan_decode(batch, max_seqlen_k, kv_dtype != SEG_ATTN_KV_BF16, num_splits, &p)) return -1;
     if (p.per_request > INT32_MAX) return -1;
     if (split_len) *split_len = p.min_len;
     return (int32_t)p.per_request;
@@ -181,9 +185,9 @@ size_t seg_attn_decode_workspace_bytes(int32_t batch, int32_t max_seqlen_k, int3
                                        int32_t num_splits) {
   try {
     if (check_heads(num_heads_q, num_heads_kv, head_dim) != SEG_ATTN_OK) return 0;
-    if (kv_dtype != SEG_ATTN_KV_BF16 && kv_dtype != SEG_ATTN_KV_FP8_E4M3) return 0;
+    if (!valid_kv_dtype(kv_dtype)) return 0;
     DecodePlan p;
-    if (!plan_decode(batch, max_seqlen_k, kv_dtype == SEG_ATTN_KV_FP8_E4M3, num_splits, &p)) return 0;
+    if (!plan_decode(batch, max_seqlen_k, kv_dtype != SEG_ATTN_KV_BF16, num_splits, &p)) return 0;
     return decode_ws_layout(batch, num_heads_q, p.per_request * batch).total;
   } catch (...) {
     return 0;
@@ -200,24 +204,24 @@ seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void*
                                   size_t workspace_bytes, seg_attn_stream_t stream) {
   try {
     if (batch < 0 || max_seqlen_k < 0 || pool_tokens < 0 || num_splits < 0) return SEG_ATTN_ERR_INVALID_ARG;
-    if (kv_dtype != SEG_ATTN_KV_BF16 && kv_dtype != SEG_ATTN_KV_FP8_E4M3) return SEG_ATTN_ERR_INVALID_ARG;
+    if (!valid_kv_dtype(kv_dtype)) return SEG_ATTN_ERR_INVALID_ARG;
     if (!std::isfinite(softmax_scale)) return SEG_ATTN_ERR_INVALID_ARG;
     seg_attn_status_t hs = check_heads(num_heads_q, num_heads_kv, head_dim);
     if (hs != SEG_ATTN_OK) return hs;
     if (pool_tokens > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
     if (batch == 0) return SEG_ATTN_OK;
-    const bool fp8 = kv_dtype == SEG_ATTN_KV_FP8_E4M3;
+    const bool scaled = kv_dtype != SEG_ATTN_KV_BF16;  // FP8 or INT8 codes with fp32 scales
     if (!q || !k_pool || !v_pool || !segs || !seg_indptr || !cu_seqlens_k || !out) return SEG_ATTN_ERR_INVALID_ARG;
-    if (fp8 && (!k_scale || !v_scale)) return SEG_ATTN_ERR_INVALID_ARG;
+    if (scaled && (!k_scale || !v_scale)) return SEG_ATTN_ERR_INVALID_ARG;
     DecodePlan p;
-    if (!plan_decode(batch, max_seqlen_k, fp8, num_splits, &p)) return SEG_ATTN_ERR_INVALID_ARG;
+    if (!plan_decode(batch, max_seqlen_k, scaled, num_splits, &p)) return SEG_ATTN_ERR_INVALID_ARG;
     const int64_t max_chunks = p.per_request * batch;
     if (max_chunks * num_heads_kv > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
     const DecodeWs lay = decode_ws_layout(batch, num_heads_q, max_chunks);
     if (workspace == nullptr || workspace_bytes < lay.total) return SEG_ATTN_ERR_WORKSPACE;
     char* ws = (char*)workspace;
     hipError_t e = segattn::launch_decode(
-        q, k_pool, v_pool, k_scale, v_scale, fp8 ? 1 : 0, segs, seg_indptr, cu_seqlens_k, batch,
+        q, k_pool, v_pool, k_scale, v_scale, kv_dtype, segs, seg_indptr, cu_seqlens_k, batch,
         num_heads_kv, p.forced_len, p.min_len, (int)max_chunks, current_cu_count(), softmax_scale, out,
         lse, (int32_t*)ws, (int32_t*)(ws + lay.base), (int32_t*)(ws + lay.tab), (float*)(ws + lay.o),
         (float*)(ws + lay.lse), (hipStream_t)stream);
@@ -237,24 +241,24 @@ seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
   try {
     if (batch < 0 || total_new < 0 || pool_tokens < 0 || num_heads_kv <= 0 || head_dim <= 0)
       return SEG_ATTN_ERR_INVALID_ARG;
-    if (kv_dtype != SEG_ATTN_KV_BF16 && kv_dtype != SEG_ATTN_KV_FP8_E4M3) return SEG_ATTN_ERR_INVALID_ARG;
+    if (!valid_kv_dtype(kv_dtype)) return SEG_ATTN_ERR_INVALID_ARG;
     if (head_dim != kHeadDim) return SEG_ATTN_ERR_UNSUPPORTED;
     if (pool_tokens > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
     if (batch == 0 && total_new > 0) return SEG_ATTN_ERR_INVALID_ARG;
     if (batch == 0 || total_new == 0) return SEG_ATTN_OK;
-    const bool fp8 = kv_dtype == SEG_ATTN_KV_FP8_E4M3;
+    const bool scaled = kv_dtype != SEG_ATTN_KV_BF16;  // FP8 or INT8 codes with fp32 scales
     if (!k_new || !v_new || !segs || !seg_indptr || !cu_seqlens_new || !cu_seqlens_k || !k_pool || !v_pool)
       return SEG_ATTN_ERR_INVALID_ARG;
-    if (fp8 && (!k_scale || !v_scale)) return SEG_ATTN_ERR_INVALID_ARG;
-    // rows move as 16-byte (bf16) or 8-byte (FP8 codes) pieces, scales as 4-byte words
+    if (scaled && (!k_scale || !v_scale)) return SEG_ATTN_ERR_INVALID_ARG;
+    // rows move as 16-byte (bf16) or 8-byte (one-byte codes) pieces, scales as 4-byte words
     auto misaligned = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
-    if (misaligned(k_new, 16) || misaligned(v_new, 16) || misaligned(k_pool, fp8 ? 8 : 16) ||
-        misaligned(v_pool, fp8 ? 8 : 16) || (fp8 && (misaligned(k_scale, 4) || misaligned(v_scale, 4))))
+    if (misaligned(k_new, 16) || misaligned(v_new, 16) || misaligned(k_pool, scaled ? 8 : 16) ||
+        misaligned(v_pool, scaled ? 8 : 16) || (scaled && (misaligned(k_scale, 4) || misaligned(v_scale, 4))))
       return SEG_ATTN_ERR_INVALID_ARG;
     if ((int64_t)total_new * num_heads_kv > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
     hipError_t e = segattn::launch_kv_append(k_new, v_new, segs, seg_indptr, cu_seqlens_new,
                                              cu_seqlens_k, batch, total_new, num_heads_kv,
-                                             pool_tokens, fp8 ? 1 : 0, k_pool, v_pool, k_scale,
+                                             pool_tokens, kv_dtype, k_pool, v_pool, k_scale,
                                              v_scale, (hipStream_t)stream);
     return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
   } catch (...) {

@@ -1,7 +1,8 @@
 // KV append: a batch's new tokens' K and V rows written into their requests' segments, the step
 // ahead of attention. Each request's cache is a few contiguous segments of one shared pool
-// (Flood README, "Introduction"); the FP8 variant quantises on write, one fp32 scale per
-// (token, kv head) row, for the FP8 KV cache of the same README's feature list.
+// (Flood README, "Introduction"); the FP8 and INT8 variants quantise on write, one fp32 scale
+// per (token, kv head) row, for the FP8 KV cache of the same README's feature list and the
+// INT8 KV cache of "FlashAttention on Ascend NPU", optimisation 3.
 //
 // Request b appends n_b = cu_new[b+1] - cu_new[b] tokens and cu_k counts its keys after the
 // append, so its new tokens are its last n_b keys, logical positions K_b - n_b .. K_b - 1.
@@ -11,7 +12,8 @@
 // the key's pool slot with its lanes working together on the tables, and stores the row there.
 // The FP8 row scale is max|x| / 448 (1 for an all-zero row); each value is divided by it in
 // fp32, correctly rounded, and converted to E4M3FN by the hardware conversion (round to
-// nearest, ties to even) after a clamp to +-448.
+// nearest, ties to even) after a clamp to +-448. INT8 is the same with 127 in place of 448 and
+// a rounding to the nearest integer, ties to even.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,6 +30,7 @@ struct Seg {
 
 constexpr int kRowsPerBlock = 16;
 constexpr float kFp8Max = 448.0f;
+constexpr float kInt8Max = 127.0f;
 
 // float pair -> two E4M3FN bytes in the low half of a word (hardware conversion, RNE)
 __device__ __forceinline__ uint32_t pack_fp8x2(float a, float b) {
@@ -97,13 +100,29 @@ __device__ __forceinline__ u32x2 encode_fp8x8(const float (&y)[8]) {
   return u32x2{w[0], w[1]};
 }
 
+// Eight quotients, clamped to +-127, rounded to the nearest integer (ties to even), as
+// two's-complement bytes (byte i = value i).
+__device__ __forceinline__ u32x2 encode_int8x8(const float (&y)[8]) {
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint32_t b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      b[q] = (uint32_t)(int)__builtin_rintf(fminf(fmaxf(y[4 * i + q], -kInt8Max), kInt8Max)) & 0xFFu;
+    w[i] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  }
+  return u32x2{w[0], w[1]};
+}
+
 // Mask of the calling lane's 16-lane group (bit i = group lane i) of a predicate.
 __device__ __forceinline__ uint32_t group_ballot(bool p) {
   const int shift = __lane_id() & 48;
   return (uint32_t)(__ballot(p) >> shift) & 0xFFFFu;
 }
 
-template <bool kFp8>
+// kFmt: 0 = bf16 pool (copy), 1 = FP8 (E4M3FN) pool, 2 = INT8 pool.
+template <int kFmt>
 __global__ __launch_bounds__(256) void kv_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const Seg* __restrict__ segs, const int32_t* __restrict__ seg_indptr,
@@ -162,7 +181,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   if (j < 0 || slot < 0 || slot >= pool_tokens) return;
 
   const int64_t dst_row = slot * hkv + h;
-  if constexpr (!kFp8) {
+  if constexpr (kFmt == 0) {
     __builtin_nontemporal_store(kraw, reinterpret_cast<u32x4*>((uint16_t*)k_pool + dst_row * 128 + 8 * sub));
     __builtin_nontemporal_store(vraw, reinterpret_cast<u32x4*>((uint16_t*)v_pool + dst_row * 128 + 8 * sub));
   } else {
@@ -178,8 +197,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     }
     ak = group_max_nonneg(ak);
     av = group_max_nonneg(av);
-    const float sk = ak > 0.f ? ak / kFp8Max : 1.0f;
-    const float sv = av > 0.f ? av / kFp8Max : 1.0f;
+    constexpr float kMax = kFmt == 1 ? kFp8Max : kInt8Max;
+    const float sk = ak > 0.f ? ak / kMax : 1.0f;
+    const float sv = av > 0.f ? av / kMax : 1.0f;
     float yk[8], yv[8];
     auto in_range = [](float s) { return s >= 0x1p-80f && s <= 0x1p80f; };
     if (in_range(sk) && in_range(sv)) {  // the same for the whole group
@@ -197,8 +217,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
       }
     }
     const int64_t dst = dst_row * 128 + 8 * sub;
-    __builtin_nontemporal_store(encode_fp8x8(yk), reinterpret_cast<u32x2*>((uint8_t*)k_pool + dst));
-    __builtin_nontemporal_store(encode_fp8x8(yv), reinterpret_cast<u32x2*>((uint8_t*)v_pool + dst));
+    const u32x2 ck = kFmt == 1 ? encode_fp8x8(yk) : encode_int8x8(yk);
+    const u32x2 cv = kFmt == 1 ? encode_fp8x8(yv) : encode_int8x8(yv);
+    __builtin_nontemporal_store(ck, reinterpret_cast<u32x2*>((uint8_t*)k_pool + dst));
+    __builtin_nontemporal_store(cv, reinterpret_cast<u32x2*>((uint8_t*)v_pool + dst));
     if (sub == 0) {
       k_scale[dst_row] = sk;
       v_scale[dst_row] = sv;
@@ -210,14 +232,14 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const void* segs,
                             const int32_t* seg_indptr, const int32_t* cu_new, const int32_t* cu_k,
-                            int batch, int total_new, int hkv, int64_t pool_tokens, int fp8,
+                            int batch, int total_new, int hkv, int64_t pool_tokens, int fmt,
                             void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                             hipStream_t stream) {
   const int64_t rows = (int64_t)total_new * hkv;
   if (rows == 0) return hipSuccess;
   if (rows > INT32_MAX) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
-  auto kern = fp8 ? kv_append_kernel<true> : kv_append_kernel<false>;
+  auto kern = fmt == 2 ? kv_append_kernel<2> : (fmt == 1 ? kv_append_kernel<1> : kv_append_kernel<0>);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, (const uint16_t*)k_new,
                      (const uint16_t*)v_new, (const Seg*)segs, seg_indptr, cu_new, cu_k, batch,
                      total_new, hkv, pool_tokens, k_pool, v_pool, k_scale, v_scale);

@@ -20,9 +20,12 @@
 // A unit that covers a whole request writes the output; otherwise it writes a partial
 // (O_s, LSE_s) for the merge pass.
 //
-// FP8 pools (OCP E4M3FN codes with one fp32 scale per token and kv head) are converted to bf16
-// exactly on the way into the MFMAs; the key scale multiplies the scores, the value scale the
-// probabilities, so the arithmetic equals bf16 attention over the dequantised pool.
+// FP8 pools (OCP E4M3FN codes with one fp32 scale per token and kv head) and INT8 pools
+// (two's-complement codes, same scales; the INT8 KV cache of "FlashAttention on Ascend NPU",
+// optimisation 3) are converted to bf16 exactly on the way into the MFMAs (every E4M3FN value
+// and every integer of magnitude <= 256 is a bf16 value); the key scale multiplies the scores,
+// the value scale the probabilities, so the arithmetic equals bf16 attention over the
+// dequantised pool.
 //
 // Merge pass: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s per (request, head).
 #include "common.hpp"
@@ -38,7 +41,8 @@ constexpr int kDecThreads = kWaves * 64;
 constexpr int kQBufs = 3;           // Q tiles of the units a wave may be working ahead into
 constexpr int kQBytes = kGroup * kHeadDim * 2;  // 2 KiB: the 8 query rows of one unit
 
-template <int kFp8>
+// kKv: 0 = bf16 pool, 1 = FP8 (E4M3FN) pool, 2 = INT8 pool; 1 and 2 share the 1-byte layout.
+template <int kKv>
 struct DecodeCfg;
 template <>
 struct DecodeCfg<0> {  // bf16: 32 keys per wave tile, 256 B rows
@@ -51,7 +55,7 @@ struct DecodeCfg<0> {  // bf16: 32 keys per wave tile, 256 B rows
   static constexpr int kCopies = 2 * (kTile / kRowsPerCopy);  // K and V copy instructions per tile
 };
 template <>
-struct DecodeCfg<1> {  // fp8: 64 keys per wave tile, 128 B rows, + k/v scales
+struct DecodeCfg<1> {  // fp8 / int8: 64 keys per wave tile, 128 B rows, + k/v scales
   static constexpr int kTile = 64;
   static constexpr int kRowBytes = 128;
   static constexpr int kChunks = 8;
@@ -60,10 +64,34 @@ struct DecodeCfg<1> {  // fp8: 64 keys per wave tile, 128 B rows, + k/v scales
   static constexpr int kScaleBytes = kTile * 4;      // 256 B each
   static constexpr int kCopies = 2 * (kTile / kRowsPerCopy) + 2;
 };
+template <>
+struct DecodeCfg<2> : DecodeCfg<1> {};
 
-template <int kFp8>
+// 8 one-byte codes (bytes 0..3 of lo, then of hi) as 8 exact bf16 values.
+template <int kKv>
+__device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  if constexpr (kKv == 1) {
+    return fp8x8_to_bf16x8(lo, hi);
+  } else {
+    // int8 -> fp32 is exact and so is the fp32 -> bf16 truncation for |c| <= 128: the value
+    // has at most 8 significant bits
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t src = i < 2 ? lo : hi;
+      const int sh = 16 * (i & 1);
+      const float f0 = (float)(int)(int8_t)(src >> sh);
+      const float f1 = (float)(int)(int8_t)(src >> (sh + 8));
+      // high halves of the two floats: bytes 2, 3 of f0 then bytes 2, 3 of f1
+      w[i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0),
+                                   0x07060302u);
+    }
+    return __builtin_bit_cast(bf16x8, w);
+  }
+}
+template <int kKv>
 struct DecodeLayout {
-  using C = DecodeCfg<kFp8>;
+  using C = DecodeCfg<kKv>;
   // one wave's stage: K tile, V tile, k scales, v scales
   static constexpr int kStageBytes = 2 * C::kKBytes + 2 * C::kScaleBytes;
   static constexpr int kCombFloats = kGroup * kHeadDim + 4 * kGroup;  // O^T, (m, l) of one wave
@@ -135,8 +163,8 @@ __device__ __forceinline__ void v_transposed(const lds_char_t* vb, int kk, bf16x
   }
 }
 
-// A operands of O^T += V^T P^T for the 32 keys 32*kk .. 32*kk + 31 of an fp8 V tile in LDS
-// (128 B rows, 16-byte chunk c of row r at c ^ (r % 8)), still as E4M3FN codes: lane
+// A operands of O^T += V^T P^T for the 32 keys 32*kk .. 32*kk + 31 of a 1-byte V tile in LDS
+// (128 B rows, 16-byte chunk c of row r at c ^ (r % 8)), still as codes: lane
 // (grp, col) gets the 8 codes V[key(j)][16*dt + col], key(j) as for the bf16 tile. The
 // transposing 8-bit read hands lane i of a 16-lane group byte i % 8 of the 8 bytes addressed by
 // lane 2*j + i / 8, so source lane s of group grp addresses row key(s / 2) at columns
@@ -490,15 +518,15 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
 
 // ------------------------------------------------------------------------------------------
 // Split pass.
-template <int kFp8>
+template <int kKv>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const bf16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale,
     const Segment* __restrict__ segs, const int32_t* __restrict__ hdr,
     const int32_t* __restrict__ recs, int hkv, float scale, float scale_log2, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, bf16_t* __restrict__ out, float* __restrict__ lse) {
-  using C = DecodeCfg<kFp8>;
-  using L = DecodeLayout<kFp8>;
+  using C = DecodeCfg<kKv>;
+  using L = DecodeLayout<kKv>;
   // Separate objects for the two stages, the combine area and the Q tiles: the compiler then
   // sees that reading one stage cannot touch the copies still landing in the other, and adds
   // no wait for them.
@@ -641,7 +669,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     for (int i = 0; i < kN; ++i) {
       const int r = C::kRowsPerCopy * i + rsub;
       int kc, vc;
-      if constexpr (kFp8 == 0) {
+      if constexpr (kKv == 0) {
         kc = cpos ^ (r & 15);
         vc = cpos ^ vswz16(r);
       } else {
@@ -652,7 +680,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       copy16_to_lds_stream(kbase + row + kc * 16, (lds_void_t*)(kb + i * 1024));
       copy16_to_lds_stream(vbase + row + vc * 16, (lds_void_t*)(vb + i * 1024));
     }
-    if constexpr (kFp8 == 1) {
+    if constexpr (kKv != 0) {
       // scales: lane L copies those of row L
       const int j = min(m.k0 + lane, last);
       int64_t s;
@@ -786,7 +814,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   auto compute = [&](const char* st, const Meta& m) __attribute__((always_inline)) {
     const lds_char_t* kb = (const lds_char_t*)st + wave * L::kStageBytes;
     const lds_char_t* vb = kb + C::kKBytes;
-    constexpr int kMt = C::kTile / 16;  // 16-key M tiles: 2 (bf16) or 4 (fp8)
+    constexpr int kMt = C::kTile / 16;  // 16-key M tiles: 2 (bf16) or 4 (fp8, int8)
     // S^T: lane holds keys 16*mt + 4*grp + i (i = 0..3) of head `col`.
     f32x4 s[kMt];
 #pragma unroll
@@ -796,7 +824,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
       for (int stp = 0; stp < 4; ++stp) {
         bf16x8 a;
-        if constexpr (kFp8 == 0) {
+        if constexpr (kKv == 0) {
           const int c = 4 * stp + grp;  // d = 32*stp + 8*grp
           a = lds_read16(kb + r * 256 + ((c ^ (r & 15)) << 4));
         } else {
@@ -804,12 +832,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
           const int c = byte >> 4;
           const __attribute__((address_space(3))) uint32_t* p =
               (const __attribute__((address_space(3))) uint32_t*)(kb + r * 128 + ((c ^ (r & 7)) << 4) + (byte & 15));
-          a = fp8x8_to_bf16x8(p[0], p[1]);
+          a = codes8_to_bf16x8<kKv>(p[0], p[1]);
         }
         s[mt] = mfma16x16x32(a, qf[stp], s[mt]);
       }
     }
-    if constexpr (kFp8 == 1) {
+    if constexpr (kKv != 0) {
 #pragma unroll
       for (int mt = 0; mt < kMt; ++mt) {
         const __attribute__((address_space(3))) f32x4* sp =
@@ -852,7 +880,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     m_run = m_new;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-    if constexpr (kFp8 == 1) {
+    if constexpr (kKv != 0) {
 #pragma unroll
       for (int mt = 0; mt < kMt; ++mt) {
         const __attribute__((address_space(3))) f32x4* sp =
@@ -866,17 +894,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     for (int kk = 0; kk < kMt / 2; ++kk) {
       bf16x8 vt[8];
       uint32_t v8lo[8], v8hi[8];
-      if constexpr (kFp8 == 0) v_transposed(vb, kk, vt);
+      if constexpr (kKv == 0) v_transposed(vb, kk, vt);
       else v_transposed8(vb, kk, v8lo, v8hi);
       bf16x8 pb = to_bf16x8(s[2 * kk][0], s[2 * kk][1], s[2 * kk][2], s[2 * kk][3], s[2 * kk + 1][0],
                             s[2 * kk + 1][1], s[2 * kk + 1][2], s[2 * kk + 1][3]);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         bf16x8 a;
-        if constexpr (kFp8 == 0) {
+        if constexpr (kKv == 0) {
           a = vt[dt];
         } else {
-          a = fp8x8_to_bf16x8(v8lo[dt], v8hi[dt]);
+          a = codes8_to_bf16x8<kKv>(v8lo[dt], v8hi[dt]);
         }
         o[dt] = mfma16x16x32(a, pb, o[dt]);
       }
@@ -997,7 +1025,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
 constexpr int kUnitsPerWorkgroup = 8;
 
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
-                         const float* k_scale, const float* v_scale, int fp8, const void* segs,
+                         const float* k_scale, const float* v_scale, int kv, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,
                          int forced_len, int min_len, int max_chunks, int cu_count, float scale,
                          void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* recs,
@@ -1014,15 +1042,10 @@ hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
   if (e != hipSuccess) return e;
   if (grid > 0) {
     const float scale_log2 = scale * 1.4426950408889634f;
-    if (fp8) {
-      hipLaunchKernelGGL(decode_split_kernel<1>, dim3(grid), dim3(kDecThreads), 0, stream,
-                         (const bf16_t*)q, k_pool, v_pool, k_scale, v_scale, (const Segment*)segs, hdr,
-                         recs, hkv, scale, scale_log2, ws_o, ws_lse, (bf16_t*)out, lse);
-    } else {
-      hipLaunchKernelGGL(decode_split_kernel<0>, dim3(grid), dim3(kDecThreads), 0, stream,
-                         (const bf16_t*)q, k_pool, v_pool, k_scale, v_scale, (const Segment*)segs, hdr,
-                         recs, hkv, scale, scale_log2, ws_o, ws_lse, (bf16_t*)out, lse);
-    }
+    auto split = kv == 2 ? decode_split_kernel<2> : (kv == 1 ? decode_split_kernel<1> : decode_split_kernel<0>);
+    hipLaunchKernelGGL(split, dim3(grid), dim3(kDecThreads), 0, stream, (const bf16_t*)q, k_pool,
+                       v_pool, k_scale, v_scale, (const Segment*)segs, hdr, recs, hkv, scale,
+                       scale_log2, ws_o, ws_lse, (bf16_t*)out, lse);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -53,17 +53,18 @@ def decode_kv_bytes(w) -> float:
     return float(w.k_lens.sum()) * per_tok
 
 
-def append_bytes(n_rows: int, fp8: bool) -> float:
+def append_bytes(n_rows: int, one_byte: bool) -> float:
     """Algorithmic HBM bytes of appending n_rows (token, kv head) rows of K and of V: the bf16
-    rows read (2 x 256 B), and either the bf16 rows written (2 x 256 B) or the FP8 codes and
-    scales written (2 x (128 + 4) B)."""
-    return float(n_rows) * (512 + (264 if fp8 else 512))
+    rows read (2 x 256 B), and either the bf16 rows written (2 x 256 B) or the FP8 / INT8 codes
+    and scales written (2 x (128 + 4) B)."""
+    return float(n_rows) * (512 + (264 if one_byte else 512))
 
 
 # The appends measured beside attention: the writes one step of a workload makes before its
 # attention call (each request's last Lq_b keys are new), with its tables and pool size.
 APPEND_CASES = (("append_chunk_bf16_4x2048", 3, "bf16"), ("append_chunk_fp8_4x2048", 3, "fp8_e4m3"),
-                ("append_decode_bf16_b128", 4, "bf16"), ("append_decode_fp8_b16", 5, "fp8_e4m3"))
+                ("append_chunk_int8_4x2048", 3, "int8"), ("append_decode_bf16_b128", 4, "bf16"),
+                ("append_decode_fp8_b16", 5, "fp8_e4m3"), ("append_decode_int8_b16", 6, "int8"))
 
 
 APPEND_REPS = 10
@@ -83,13 +84,14 @@ def measure_append(name, c, fmt, steps, warmup, dev):
     shape = (total, w.num_heads_kv, w.head_dim)
     k_new = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
     v_new = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
-    fp8 = fmt == "fp8_e4m3"
-    if fp8 == (w.kv_dtype == "fp8_e4m3"):
+    one_byte = fmt != "bf16"
+    if fmt == w.kv_dtype:
         kp, vp, ks, vs = w.k_pool, w.v_pool, w.k_scale, w.v_scale
-    else:  # same tables, the other pool format (the append never reads the pool)
+    else:  # same tables, another pool format (the append never reads the pool)
         pshape = tuple(w.k_pool.shape)
-        kp = torch.zeros(pshape, dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn)
-        vp = torch.zeros(pshape, dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn)
+        pdt = torch.float8_e4m3fn if fmt == "fp8_e4m3" else torch.int8
+        kp = torch.zeros(pshape, dtype=torch.uint8, device=dev).view(pdt)
+        vp = torch.zeros(pshape, dtype=torch.uint8, device=dev).view(pdt)
         ks = torch.ones(pshape[:2], dtype=torch.float32, device=dev)
         vs = torch.ones(pshape[:2], dtype=torch.float32, device=dev)
 
@@ -103,7 +105,7 @@ def measure_append(name, c, fmt, steps, warmup, dev):
     t = time_steps(step, steps, warmup, graph=True)
     t["launch_ms_mean"] /= APPEND_REPS
     t["ms_per_step"] /= APPEND_REPS
-    work = append_bytes(total * w.num_heads_kv, fp8)
+    work = append_bytes(total * w.num_heads_kv, one_byte)
     achieved = work / (t["launch_ms_mean"] * 1e-3) / 1e9
     rf = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
           "frac": achieved / PEAK_HBM_GBS, "traffic": load_traffic("append", name)}
@@ -125,7 +127,7 @@ def make_step(w):
                        out=out)
         return step
     out = torch.empty_like(w.q)
-    kvd = sa.KV_FP8_E4M3 if w.kv_dtype == "fp8_e4m3" else sa.KV_BF16
+    kvd = {"bf16": sa.KV_BF16, "fp8_e4m3": sa.KV_FP8_E4M3, "int8": sa.KV_INT8}[w.kv_dtype]
     need = sa.decode_workspace_bytes(w.batch, w.max_seqlen_k, w.num_heads_q, w.num_heads_kv, w.head_dim, kvd, 0)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.q.device)
 
@@ -241,7 +243,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--config", type=int, default=2, help="headline workload (1..5)")
+    ap.add_argument("--config", type=int, default=2, help="headline workload (1..6)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph capturing one step instead of eager calls")
     ap.add_argument("--append-only", default=None, metavar="NAME|all",
@@ -308,7 +310,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8_e4m3 kv / bf16 mfma",
+        "dtype": "bf16" if w.kv_dtype == "bf16" else f"{w.kv_dtype} kv / bf16 mfma",
         "data": "synthetic",
         "config": {"workload": w.name, "recipe": w.recipe, "batch": w.batch,
                    "q_len": int(w.q_lens.max()), "k_len": int(w.k_lens.max()), "heads_q": w.num_heads_q,
@@ -321,7 +323,7 @@ def main():
 
     if not args.quick:
         extra = []
-        for c in (1, 2, 3, 4, 5):
+        for c in (1, 2, 3, 4, 5, 6):
             if c == head_c:
                 continue
             log(f"[bench] config {c}: generating")

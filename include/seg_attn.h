@@ -25,10 +25,10 @@
  *             crosses the ABI. The device-resident tables (segments, cu_seqlens) are trusted on
  *             the hot path: check them with seg_attn_validate_tables on host copies if needed.
  * Layouts:    q / out          [total_q, Hq, D]   bf16, row-major, contiguous
- *             k_pool / v_pool  [pool_tokens, Hkv, D] bf16 or fp8 (OCP E4M3FN), contiguous:
- *                              each (token, kv head) row is D contiguous elements
- *             k_scale/v_scale  [pool_tokens, Hkv]  fp32, FP8 pools only: a stored code c at
- *                              (token, head) means the value c * scale[token, head]
+ *             k_pool / v_pool  [pool_tokens, Hkv, D] bf16, fp8 (OCP E4M3FN) or int8,
+ *                              contiguous: each (token, kv head) row is D contiguous elements
+ *             k_scale/v_scale  [pool_tokens, Hkv]  fp32, FP8 and INT8 pools only: a stored
+ *                              code c at (token, head) means c * scale[token, head]
  *             lse              [total_q, Hq] fp32, natural log; -inf for a row with no key
  *             segs             [nseg] seg_attn_segment_t; request b owns
  *                              segs[seg_indptr[b] .. seg_indptr[b+1]) and its logical keys are
@@ -72,7 +72,10 @@ enum {
   SEG_ATTN_ERR_TABLE = 5        /* seg_attn_validate_tables found an inconsistent table */
 };
 
-enum { SEG_ATTN_KV_BF16 = 0, SEG_ATTN_KV_FP8_E4M3 = 1 };
+/* KV pool formats. FP8 and INT8 pools hold one-byte codes plus one fp32 scale per (token, kv
+ * head) row; a code c at (token, head) means c * scale[token, head]. INT8 codes are two's
+ * complement (the INT8 KV cache of "FlashAttention on Ascend NPU", optimisation 3). */
+enum { SEG_ATTN_KV_BF16 = 0, SEG_ATTN_KV_FP8_E4M3 = 1, SEG_ATTN_KV_INT8 = 2 };
 
 /*
  * Prefill: attention of a batch of query chunks against their requests' segmented KV.
@@ -101,11 +104,13 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
  *
  * q            [batch, Hq, 128] bf16.
  * k_pool/v_pool[pool_tokens, Hkv, 128]: bf16 when kv_dtype == SEG_ATTN_KV_BF16, E4M3FN codes
- *              (1 byte each) when kv_dtype == SEG_ATTN_KV_FP8_E4M3.
- * k_scale/v_scale [pool_tokens, Hkv] fp32 for FP8 (required), ignored (may be NULL) for bf16.
+ *              when SEG_ATTN_KV_FP8_E4M3, int8 codes when SEG_ATTN_KV_INT8 (1 byte each).
+ * k_scale/v_scale [pool_tokens, Hkv] fp32 for FP8 and INT8 (required), ignored (may be NULL)
+ *              for bf16. Codes are converted to bf16 exactly; k_scale multiplies the fp32
+ *              scores and v_scale the fp32 probabilities before their bf16 rounding.
  * cu_seqlens_k [batch+1] int32; max_seqlen_k: HOST upper bound of K_b.
  * num_splits   0: each request's keys are cut into chunks whose length the device picks from the
- *              total key count (at least 512 keys for bf16, 1024 for fp8) so that every compute
+ *              total key count (at least 512 keys for bf16, 1024 for fp8 / int8) so that every compute
  *              unit gets several (chunk, kv head) work units. n > 0: chunks of
  *              ceil(max_seqlen_k / n) keys rounded up to a multiple of 64, so at most n per
  *              request. A request cut into one chunk is written directly; otherwise each chunk's
@@ -161,11 +166,14 @@ int32_t seg_attn_decode_num_splits(int32_t batch, int32_t max_seqlen_k, int32_t 
  *              (token, kv head) row x the scale s = max|x| / 448 in fp32 (1 for an all-zero row)
  *              goes to k_scale/v_scale[slot, head] and the codes E4M3FN(clamp(x / s, +-448)),
  *              x / s an fp32 division and the conversion rounding to nearest, ties to even, go
- *              to the pool; the largest |x| of a row is stored as +-448.
- * k_pool/v_pool[pool_tokens, Hkv, 128] bf16 or E4M3FN bytes; k_scale/v_scale [pool_tokens, Hkv]
- *              fp32 for FP8 (required), ignored for bf16. Only the new tokens' slots (and their
+ *              to the pool; the largest |x| of a row is stored as +-448. SEG_ATTN_KV_INT8: the
+ *              same with s = max|x| / 127 and codes round-half-even(clamp(x / s, +-127)) as
+ *              two's-complement bytes (-128 is never written).
+ *              New rows must be finite.
+ * k_pool/v_pool[pool_tokens, Hkv, 128] bf16, E4M3FN or int8 bytes; k_scale/v_scale
+ *              [pool_tokens, Hkv] fp32 for FP8 and INT8 (required), ignored for bf16. Only the new tokens' slots (and their
  *              scales) are written; every other slot is left as it was.
- * k_new, v_new and bf16 pools must be 16-byte aligned, FP8 pools 8-byte, scales 4-byte
+ * k_new, v_new and bf16 pools must be 16-byte aligned, FP8 / INT8 pools 8-byte, scales 4-byte
  * (SEG_ATTN_ERR_INVALID_ARG otherwise); torch and hipMalloc allocations are.
  * A key whose slot falls outside the request's segments or the pool is skipped, never written
  * out of bounds; this only happens with tables that break the rules above. New tokens of

@@ -83,7 +83,7 @@ def _decode_args(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(q=None), 1), (dict(kvd=7), 1), (dict(kvd=1), 1), (dict(kvd=1, ks=1), 1), (dict(d=96), 2),
     (dict(ns=-1), 1), (dict(mk=-1), 1), (dict(ns=4), 3), (dict(ns=4, ws=1, wsb=16), 3),
-    (dict(ns=0), 3), (dict(ns=1), 3),
+    (dict(ns=0), 3), (dict(ns=1), 3), (dict(kvd=2), 1), (dict(kvd=2, vs=1), 1), (dict(kvd=3), 1),
 ])
 def test_decode_rejects_bad_arguments(over, status):
     lib = _lib()
@@ -105,6 +105,7 @@ def _append_args(**over):
     (dict(hkv=0), 1), (dict(pool=-1), 1), (dict(kvd=3), 1), (dict(kvd=1), 1), (dict(kvd=1, ks=1), 1),
     (dict(d=64), 2), (dict(pool=2 ** 31), 2), (dict(batch=0), 1),
     (dict(kn=16 + 8), 1), (dict(kp=2), 1), (dict(kvd=1, ks=4, vs=6, kp=8, vp=16), 1),
+    (dict(kvd=2), 1), (dict(kvd=2, ks=4, vs=8, kp=4, vp=8), 1),
     (dict(vn=264), 1),
 ])
 def test_kv_append_rejects_bad_arguments(over, status):
@@ -133,6 +134,12 @@ def test_split_plan_and_workspace_size():
         # plan header + chunk offsets + chunk records + one (O, LSE) partial per chunk and head
         assert ws >= 256 + (bsz + 1) * 4 + bsz * n * 64 + bsz * 64 * n * (128 + 1) * 4
     assert sa.decode_workspace_bytes(4, 1000, 64, 8, 64, 0, 4) == 0  # unsupported head dim
+    # one-byte formats share the plan: FP8 and INT8 chunks are at least 1024 keys
+    assert sa.decode_num_splits(16, 131072, 8, sa.KV_INT8, 0) == sa.decode_num_splits(16, 131072, 8, sa.KV_FP8_E4M3, 0)
+    assert sa.decode_num_splits(16, 131072, 8, sa.KV_INT8, 0)[1] == 1024
+    assert sa.decode_workspace_bytes(16, 131072, 64, 8, 128, sa.KV_INT8, 0) == \
+        sa.decode_workspace_bytes(16, 131072, 64, 8, 128, sa.KV_FP8_E4M3, 0)
+    assert sa.decode_workspace_bytes(16, 1000, 64, 8, 128, 3, 0) == 0
 
 
 def test_validate_tables_accepts_good_and_flags_bad():

@@ -63,17 +63,17 @@ def _run_append(w, k_new, v_new, cu_new):
 
 def _compare_whole(w, k_new, v_new, n_new, name):
     segs, ind, ck, cu_new = _tables_and_counts(w, n_new)
-    fp8 = w.kv_dtype == "fp8_e4m3"
+    scaled = w.kv_dtype in ("fp8_e4m3", "int8")
     kp0, vp0 = _raw(w.k_pool), _raw(w.v_pool)
-    ks0 = _raw(w.k_scale).view(np.float32) if fp8 else None
-    vs0 = _raw(w.v_scale).view(np.float32) if fp8 else None
+    ks0 = _raw(w.k_scale).view(np.float32) if scaled else None
+    vs0 = _raw(w.v_scale).view(np.float32) if scaled else None
     kp, vp, ks, vs = oracle.kv_append(wl.bits(k_new), wl.bits(v_new), segs, ind, cu_new, ck, kp0, vp0,
                                       ks0, vs0, fmt=w.kv_dtype)
     _run_append(w, k_new, v_new, cu_new)
     torch.cuda.synchronize()
     assert np.array_equal(_raw(w.k_pool), kp), f"{name}: k_pool differs"
     assert np.array_equal(_raw(w.v_pool), vp), f"{name}: v_pool differs"
-    if fp8:
+    if scaled:
         assert np.array_equal(_raw(w.k_scale), ks.view(np.uint32)), f"{name}: k_scale differs"
         assert np.array_equal(_raw(w.v_scale), vs.view(np.uint32)), f"{name}: v_scale differs"
     print(f"[parity] append {name}: {int(cu_new[-1])} tokens, pools bit-exact", flush=True)
@@ -81,7 +81,7 @@ def _compare_whole(w, k_new, v_new, n_new, name):
 
 
 @needs_gpu
-@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3", "int8"])
 def test_append_decode_step_small(fmt):
     """One new token per request (a few requests append none), 1-4 segments with empty ones."""
     print(f"[case] append decode step {fmt}", flush=True)
@@ -98,7 +98,7 @@ def test_append_decode_step_small(fmt):
 
 
 @needs_gpu
-@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3", "int8"])
 def test_append_prefill_chunks_ragged(fmt):
     """Ragged chunks: none, one token, a chunk spanning segment boundaries, a whole request,
     a chunk not a multiple of 16 rows, and a request with no keys at all."""
@@ -115,26 +115,27 @@ def test_append_prefill_chunks_ragged(fmt):
 @needs_gpu
 def test_append_other_kv_head_counts():
     """Hkv = 1 and Hkv = 3: the (token, head) row index and the slot stride follow Hkv."""
-    for hkv, seed in ((1, 31), (3, 32)):
+    for hkv, seed, fmt in ((1, 31, "fp8_e4m3"), (3, 32, "fp8_e4m3"), (3, 33, "int8")):
         print(f"[case] append hkv={hkv}", flush=True)
         k_lens = [40, 90, 17]
         n_new = np.array([40, 3, 16], dtype=np.int64)
         w = wl.make_random(seed, batch=3, q_lens=[1] * 3, k_lens=k_lens, max_segs=3, kind="decode",
-                           kv_dtype="fp8_e4m3", num_heads_q=8 * hkv, num_heads_kv=hkv, device="cuda")
+                           kv_dtype=fmt, num_heads_q=8 * hkv, num_heads_kv=hkv, device="cuda")
         k_new = _new_rows(seed + 1, int(n_new.sum()), hkv=hkv)
         v_new = _new_rows(seed + 2, int(n_new.sum()), hkv=hkv)
-        _compare_whole(w, k_new, v_new, n_new, f"hkv={hkv}")
+        _compare_whole(w, k_new, v_new, n_new, f"hkv={hkv} {fmt}")
 
 
 @needs_gpu
-def test_append_then_decode_reads_what_was_written():
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "int8"])
+def test_append_then_decode_reads_what_was_written(fmt):
     """Appending a request's last token, then decoding, gives what the attention oracle gives on
     the pool the append oracle produced: the formats of the two steps agree."""
-    print("[case] append then decode fp8", flush=True)
+    print(f"[case] append then decode {fmt}", flush=True)
     from tests import _helpers as H
     k_lens = [300, 1500, 64, 2047]
     w = wl.make_random(41, batch=4, q_lens=[1] * 4, k_lens=k_lens, max_segs=3, kind="decode",
-                       kv_dtype="fp8_e4m3", device="cuda")
+                       kv_dtype=fmt, device="cuda")
     n_new = np.ones(4, dtype=np.int64)
     k_new, v_new = _new_rows(42, 4, special=False), _new_rows(43, 4, special=False)
     h = H.host_inputs(w)
@@ -150,14 +151,18 @@ def test_append_then_decode_reads_what_was_written():
 
 def _full_size_case(c, fmt=None):
     """The append a step of named workload c performs: each request's last Lq_b keys are new
-    (one per request for decode, the whole chunk for prefill). With ``fmt`` = "fp8_e4m3" a bf16
-    workload's pools are replaced by NaN-poisoned FP8 pools of the same shape (the append reads
-    only the tables)."""
+    (one per request for decode, the whole chunk for prefill). With ``fmt`` = "fp8_e4m3" or
+    "int8" a bf16 workload's pools are replaced by poisoned pools of that format and the same
+    shape (NaN codes, or -128, and NaN scales; the append reads only the tables)."""
     w = wl.make_config(c, device="cuda")
-    if fmt == "fp8_e4m3" and w.kv_dtype != fmt:
+    if fmt in ("fp8_e4m3", "int8") and w.kv_dtype != fmt:
         shape = tuple(w.k_pool.shape)
-        w.k_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
-        w.v_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+        if fmt == "fp8_e4m3":
+            w.k_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+            w.v_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+        else:
+            w.k_pool = torch.full(shape, -128, dtype=torch.int8, device="cuda")
+            w.v_pool = torch.full(shape, -128, dtype=torch.int8, device="cuda")
         w.k_scale = torch.full(shape[:2], float("nan"), dtype=torch.float32, device="cuda")
         w.v_scale = torch.full(shape[:2], float("nan"), dtype=torch.float32, device="cuda")
         w.kv_dtype = fmt
@@ -166,7 +171,8 @@ def _full_size_case(c, fmt=None):
 
 
 @needs_gpu
-@pytest.mark.parametrize("c,fmt", [(2, None), (3, None), (3, "fp8_e4m3"), (4, None), (5, None)])
+@pytest.mark.parametrize("c,fmt", [(2, None), (3, None), (3, "fp8_e4m3"), (3, "int8"), (4, None), (5, None),
+                                   (6, None)])
 def test_append_full_size_workloads(c, fmt):
     print(f"[case] append at config {c} size, {fmt or 'its own'} pool", flush=True)
     w, n_new = _full_size_case(c, fmt)
@@ -183,11 +189,12 @@ def test_append_full_size_workloads(c, fmt):
     _run_append(w, k_new, v_new, cu_new)
     torch.cuda.synchronize()
     idx = torch.as_tensor(slots, device="cuda")
-    fp8 = w.kv_dtype == "fp8_e4m3"
+    scaled = w.kv_dtype in ("fp8_e4m3", "int8")
+    quant = oracle.quantize_rows if w.kv_dtype == "fp8_e4m3" else oracle.quantize_rows_int8
     for pool, scale, new, nm in ((w.k_pool, w.k_scale, k_new, "k"), (w.v_pool, w.v_scale, v_new, "v")):
         got = _raw(pool[idx])
-        if fp8:
-            codes, sc = oracle.quantize_rows(oracle.bf16_bits_to_f32(wl.bits(new)))
+        if scaled:
+            codes, sc = quant(oracle.bf16_bits_to_f32(wl.bits(new)))
             assert np.array_equal(got, codes), f"config {c}: {nm} codes differ"
             assert np.array_equal(_raw(scale[idx]), sc.view(np.uint32)), f"config {c}: {nm} scales differ"
         else:
@@ -195,7 +202,7 @@ def test_append_full_size_workloads(c, fmt):
     # every other slot kept its bits (compared on the device: the pools are up to 2 GiB)
     keep = torch.ones(w.pool_tokens, dtype=torch.bool, device="cuda")
     keep[idx] = False
-    after = [w.k_pool, w.v_pool] + ([w.k_scale, w.v_scale] if fp8 else [])
+    after = [w.k_pool, w.v_pool] + ([w.k_scale, w.v_scale] if scaled else [])
     for a, b in zip(after, before):
         ai = a.view(torch.uint8) if a.element_size() == 1 else a.view(torch.int16 if a.element_size() == 2 else torch.int32)
         bi = b.view(torch.uint8) if b.element_size() == 1 else b.view(torch.int16 if b.element_size() == 2 else torch.int32)

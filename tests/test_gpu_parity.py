@@ -106,6 +106,22 @@ def test_config5_fp8_decode_sampled():
     _report("config5 (64 rows)", mx, rms)
 
 
+@needs_gpu
+def test_config6_int8_decode_sampled():
+    print("[case] config 6 decode int8 (sampled rows)", flush=True)
+    w = wl.make_config(6, device="cuda")
+    out, lse = H.run_gpu(w)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(6)
+    rows = [(b, 0, int(h)) for b in range(w.batch) for h in rng.choice(64, size=4, replace=False)]
+    o_ref, l_ref = H.oracle_rows(w, rows)
+    mx, rms = H.assert_close(H.gather_rows(out, w, rows), o_ref, "config6")
+    got_l = np.array([lse[b, h].item() for b, _, h in rows])
+    H.assert_lse_close(got_l, l_ref, "config6")
+    _report("config6 (64 rows)", mx, rms)
+
+
 # ---------------------------------------------------------------- ragged and edge cases
 
 RAGGED_PREFILL = [
@@ -156,6 +172,9 @@ RAGGED_DECODE = [
     (26, [1, 100, 2000, 9000], 6, "fp8_e4m3", 0),
     (27, [1, 100, 2000, 9000], 6, "fp8_e4m3", 1),
     (28, [3000, 129], 8, "fp8_e4m3", 5),
+    (29, [1, 100, 2000, 9000], 6, "int8", 0),
+    (30, [3000, 129, 64], 8, "int8", 5),
+    (31, [0, 7, 1500], 3, "int8", 1),
 ]
 
 
@@ -170,7 +189,7 @@ def test_decode_ragged_full(case):
 
 
 @needs_gpu
-@pytest.mark.parametrize("batch,kvd", [(512, "bf16"), (513, "bf16"), (700, "fp8_e4m3")])
+@pytest.mark.parametrize("batch,kvd", [(512, "bf16"), (513, "bf16"), (700, "fp8_e4m3"), (600, "int8")])
 def test_decode_large_batches(batch, kvd):
     """The decode plan spreads each request's chunks over several threads up to 512 requests and
     walks them one thread per request above that: both sides of the boundary, short requests in
