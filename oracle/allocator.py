@@ -8,15 +8,22 @@ fixed-size pages, to keep the cache of a request contiguous (Flood README, "Intr
 The pages say nothing about how those segments are handed out; the policy modelled here (and
 implemented by the library) is the plainest one that serves that aim:
 
-- growing a request by n tokens first extends its last segment in place, over the free slots
-  that directly follow it;
-- the remaining m tokens go into the smallest free run of at least m slots (lowest start among
-  equals), taken from the run's start;
-- if no free run holds m slots, the largest free run (lowest start among equals) is taken whole
-  and the rest is placed the same way, again and again;
-- a grow that does not fit in the free slots fails and changes nothing;
-- releasing a request frees all its slots; truncating it to L keys frees its keys L, L+1, ...;
-- a request's keys are its segments in the order they were added.
+- a request owns segments, in the order they were added, holding C slots (its capacity); its
+  L keys (L <= C) are the first L of those slots, and the tables list only them;
+- growing a request by n tokens uses its spare capacity first; a shortfall of m slots is
+  allocated as below, aiming at w = m rounded up to the allocator's granule G (w = m if fewer
+  than w slots are free), so that a request growing one token at a time gets a new range only
+  every G tokens;
+- reserving capacity c allocates c - C slots the same way (w = c - C) without adding keys, for
+  a caller that knows a request's final length;
+- an allocation of w slots (at least m of them needed) first extends the last segment in place,
+  over up to w of the free slots that directly follow it; the remaining w' (m') go into the
+  smallest free run of at least w' slots (lowest start among equals), taken from its start; if no
+  free run holds w', the largest free run (lowest start among equals) gives min(its length, w')
+  slots and the rest is placed the same way, until at least m slots were added;
+- an allocation that needs more slots than are free fails and changes nothing;
+- releasing a request frees all its slots; truncating it to L' < L keys frees every slot after
+  its first L' (spare capacity included).
 
 The model keeps one boolean per pool slot and finds free runs by scanning it, so that it can be
 checked by eye; it is slow and meant for small pools.
@@ -31,12 +38,14 @@ import numpy as np
 class AllocatorModel:
     """Bitmap model: used[i] is True when pool slot i belongs to some request."""
 
-    def __init__(self, pool_tokens: int):
-        if pool_tokens < 0:
-            raise ValueError("pool_tokens must be >= 0")
+    def __init__(self, pool_tokens: int, granule: int = 1):
+        if pool_tokens < 0 or granule < 1:
+            raise ValueError("pool_tokens must be >= 0 and granule >= 1")
         self.pool_tokens = int(pool_tokens)
+        self.granule = int(granule)
         self.used = np.zeros(self.pool_tokens, dtype=bool)
-        self.segs: Dict[int, List[List[int]]] = {}  # request -> [[offset, length], ...]
+        self.segs: Dict[int, List[List[int]]] = {}  # request -> [[offset, slots], ...]
+        self.keys: Dict[int, int] = {}               # request -> L
 
     # ---------------------------------------------------------------- queries
 
@@ -60,9 +69,23 @@ class AllocatorModel:
         return int(self.pool_tokens - self.used.sum())
 
     def length(self, request: int) -> int:
+        return self.keys.get(request, 0)
+
+    def capacity(self, request: int) -> int:
         return sum(ln for _, ln in self.segs.get(request, []))
 
     def segments(self, request: int) -> List[Tuple[int, int]]:
+        """The segments holding the request's keys: its first L slots, in order."""
+        out, left = [], self.length(request)
+        for o, ln in self.segs.get(request, []):
+            if left <= 0:
+                break
+            out.append((o, min(ln, left)))
+            left -= ln
+        return out
+
+    def owned(self, request: int) -> List[Tuple[int, int]]:
+        """Every slot range the request owns, spare capacity included."""
         return [(o, ln) for o, ln in self.segs.get(request, [])]
 
     # ---------------------------------------------------------------- updates
@@ -71,49 +94,79 @@ class AllocatorModel:
         assert not self.used[start:start + n].any()
         self.used[start:start + n] = True
 
-    def grow(self, request: int, n: int) -> bool:
-        """Add n tokens to the request; False (and no change) if the pool cannot hold them."""
-        if n < 0:
-            raise ValueError("n must be >= 0")
-        if n > self.free_tokens():
-            return False
+    def _allocate(self, request: int, need: int, want: int):
+        """Add at least `need` (aiming at `want`) slots to the request; need <= free slots."""
         segs = self.segs.setdefault(request, [])
-        left = n
+        if want > self.free_tokens():
+            want = need
         # 1. in place, after the last segment
-        if segs and left > 0:
+        if segs and want > 0:
             end = segs[-1][0] + segs[-1][1]
             k = 0
-            while k < left and end + k < self.pool_tokens and not self.used[end + k]:
+            while k < want and end + k < self.pool_tokens and not self.used[end + k]:
                 k += 1
             if k > 0:
                 self._take(end, k)
                 segs[-1][1] += k
-                left -= k
-        # 2./3. best fit, else the largest run whole, repeatedly
-        while left > 0:
+                need -= k
+                want -= k
+        # 2./3. best fit for what is still wanted, else the largest run, until enough
+        while need > 0:
             runs = self.free_runs()
-            fits = [r for r in runs if r[1] >= left]
+            fits = [r for r in runs if r[1] >= want]
             if fits:
                 start, _ = min(fits, key=lambda r: (r[1], r[0]))
-                take = left
+                take = want
             else:
                 start, ln = min(runs, key=lambda r: (-r[1], r[0]))
-                take = ln
+                take = min(ln, want)
             self._take(start, take)
             segs.append([start, take])
-            left -= take
+            need -= take
+            want -= take
+
+    def _round(self, m: int) -> int:
+        return -(-m // self.granule) * self.granule
+
+    def grow(self, request: int, n: int) -> bool:
+        """Add n keys to the request; False (and no change) if the pool cannot hold them."""
+        if n < 0:
+            raise ValueError("n must be >= 0")
+        short = self.length(request) + n - self.capacity(request)
+        if short > self.free_tokens():
+            return False
+        self.segs.setdefault(request, [])
+        if short > 0:
+            self._allocate(request, short, self._round(short))
+        self.keys[request] = self.length(request) + n
+        return True
+
+    def reserve(self, request: int, capacity: int) -> bool:
+        """Make the request's capacity at least `capacity`; False (no change) if it cannot."""
+        if capacity < 0:
+            raise ValueError("capacity must be >= 0")
+        short = capacity - self.capacity(request)
+        if short > self.free_tokens():
+            return False
+        self.segs.setdefault(request, [])
+        self.keys.setdefault(request, 0)
+        if short > 0:
+            self._allocate(request, short, short)
         return True
 
     def release(self, request: int):
         for off, ln in self.segs.pop(request, []):
             self.used[off:off + ln] = False
+        self.keys.pop(request, None)
 
     def truncate(self, request: int, new_length: int):
-        """Keep the request's first new_length keys and free the rest."""
+        """Keep the request's first new_length keys and free every later slot it owns."""
         if new_length < 0:
             raise ValueError("new_length must be >= 0")
-        segs = self.segs.get(request, [])
-        excess = self.length(request) - new_length
+        if request not in self.segs or new_length >= self.length(request):
+            return
+        segs = self.segs[request]
+        excess = self.capacity(request) - new_length
         while excess > 0 and segs:
             off, ln = segs[-1]
             cut = min(excess, ln)
@@ -122,6 +175,7 @@ class AllocatorModel:
             if segs[-1][1] == 0:
                 segs.pop()
             excess -= cut
+        self.keys[request] = new_length
 
     # ---------------------------------------------------------------- tables
 

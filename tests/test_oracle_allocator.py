@@ -54,6 +54,42 @@ def test_hand_worked_truncate_and_tables():
     assert a.segments(7) == [] and a.free_tokens() == 14
 
 
+def test_hand_worked_granule():
+    a = AllocatorModel(20, granule=4)
+    assert a.grow(1, 1) and a.owned(1) == [(0, 4)] and a.segments(1) == [(0, 1)]
+    assert a.grow(2, 1) and a.owned(2) == [(4, 4)]
+    # spare capacity first: no new range
+    assert a.grow(1, 3) and a.owned(1) == [(0, 4)] and a.segments(1) == [(0, 4)]
+    # one more key: slot 4 is request 2's, so a new range of 4 from the best (only) run
+    assert a.grow(1, 1) and a.owned(1) == [(0, 4), (8, 4)] and a.segments(1) == [(0, 4), (8, 1)]
+    # 8 slots free; a shortfall of 7 rounds up to 8 = all of them; one more fails
+    assert a.grow(3, 7) and a.owned(3) == [(12, 8)] and a.segments(3) == [(12, 7)]
+    assert a.free_tokens() == 0 and a.grow(3, 1) and not a.grow(3, 1)
+    # rounding is dropped when it does not fit: 1 free slot, shortfall 1
+    a.release(2)
+    assert a.grow(4, 3) and a.owned(4) == [(4, 4)] and a.segments(4) == [(4, 3)]
+
+
+def test_hand_worked_reserve():
+    a = AllocatorModel(20)
+    assert a.reserve(5, 10) and a.owned(5) == [(0, 10)] and a.segments(5) == []
+    assert a.tables([5])[2].tolist() == [0, 0]
+    assert a.grow(5, 3) and a.segments(5) == [(0, 3)] and a.owned(5) == [(0, 10)]
+    assert a.grow(6, 4) and a.owned(6) == [(10, 4)]
+    # 7 spare slots, 8 asked: one more slot, slot 10 is taken, so from the only free run
+    assert a.grow(5, 8) and a.segments(5) == [(0, 10), (14, 1)]
+    # reserving less than the capacity changes nothing; more than the free slots fails
+    assert a.reserve(5, 4) and a.owned(5) == [(0, 10), (14, 1)]
+    assert not a.reserve(5, 11 + 6) and a.owned(5) == [(0, 10), (14, 1)]
+    # truncation frees spare capacity too
+    a.truncate(5, 2)
+    assert a.owned(5) == [(0, 2)] and a.free_runs() == [(2, 8), (14, 6)]
+    # truncating to more than the keys keeps everything
+    assert a.reserve(5, 6) and a.owned(5) == [(0, 6)]
+    a.truncate(5, 5)
+    assert a.owned(5) == [(0, 6)] and a.length(5) == 2
+
+
 def _check_invariants(a: AllocatorModel, lengths):
     owner = np.full(a.pool_tokens, -1)
     for r, segs in a.segs.items():
@@ -63,9 +99,12 @@ def _check_invariants(a: AllocatorModel, lengths):
             assert (owner[off:off + ln] == -1).all(), "two segments share a slot"
             owner[off:off + ln] = r
             total += ln
-        assert total == lengths.get(r, 0)
+        assert total == a.capacity(r) >= lengths.get(r, 0)
+        assert sum(ln for _, ln in a.segments(r)) == lengths.get(r, 0)
+        if a.granule == 1 and r not in a.reserved:
+            assert total == lengths.get(r, 0)
     assert np.array_equal(owner >= 0, a.used)
-    assert a.free_tokens() == a.pool_tokens - sum(lengths.values())
+    assert a.free_tokens() == a.pool_tokens - sum(a.capacity(r) for r in a.segs)
     # free runs are maximal, disjoint and cover exactly the unused slots
     cover = np.zeros(a.pool_tokens, dtype=bool)
     for s, ln in a.free_runs():
@@ -76,33 +115,61 @@ def _check_invariants(a: AllocatorModel, lengths):
     assert np.array_equal(cover, ~a.used)
 
 
-@pytest.mark.parametrize("seed", range(4))
-def test_random_sequences_keep_the_invariants(seed):
+@pytest.mark.parametrize("seed,granule,reserve", [(0, 1, False), (1, 1, False), (2, 1, True),
+                                                  (3, 8, False), (4, 8, True), (5, 64, True)])
+def test_random_sequences_keep_the_invariants(seed, granule, reserve):
     rng = np.random.default_rng(seed)
-    a = AllocatorModel(400)
+    a = AllocatorModel(400, granule=granule)
+    a.reserved = set()
     lengths = {}
     for _ in range(600):
         op = rng.random()
         r = int(rng.integers(0, 12))
-        if op < 0.6:
+        if op < 0.5 or (op < 0.6 and not reserve):
             n = int(rng.integers(0, 60))
+            short = lengths.get(r, 0) + n - a.capacity(r)
             free = a.free_tokens()
             ok = a.grow(r, n)
-            assert ok == (n <= free)
+            assert ok == (short <= free)
             if ok:
                 lengths[r] = lengths.get(r, 0) + n
+        elif op < 0.6:
+            c = int(rng.integers(0, 120))
+            ok = a.reserve(r, c)
+            assert ok == (c - a.capacity(r) <= a.free_tokens()) or not ok
+            if ok:
+                a.reserved.add(r)
+                lengths.setdefault(r, 0)
+                assert a.capacity(r) >= c
         elif op < 0.8:
             a.release(r)
             lengths.pop(r, None)
+            a.reserved.discard(r)
         else:
             keep = int(rng.integers(0, lengths.get(r, 0) + 1))
             a.truncate(r, keep)
             if r in lengths:
+                if keep < lengths[r]:
+                    a.reserved.discard(r)
                 lengths[r] = keep
         _check_invariants(a, lengths)
     for r in list(a.segs):
         a.release(r)
     assert a.free_runs() == [(0, 400)]
+
+
+def test_granule_bounds_the_segments_of_interleaved_growth():
+    # 32 requests growing one key at a time in turn: with granule G each request gets a new
+    # range at most every G keys
+    for g in (1, 16, 64):
+        a = AllocatorModel(32 * 300, granule=g)
+        for _ in range(160):
+            for r in range(32):
+                assert a.grow(r, 1)
+        worst = max(len(a.segments(r)) for r in range(32))
+        assert worst <= -(-160 // g)
+        if g == 1:
+            assert worst == 160  # every neighbour blocks in-place growth
 
 
 def test_in_place_extension_is_taken_whenever_possible():
