@@ -10,6 +10,8 @@ kernels. If the library has not been built, every call raises.
                  k_scale=None, v_scale=None)
     kv_append(k_new, v_new, segs, seg_indptr, cu_seqlens_new, cu_seqlens_k, k_pool, v_pool,
               k_scale=None, v_scale=None)
+    alloc = SegmentAllocator(pool_tokens); alloc.grow(request, n)
+    segs, seg_indptr, cu_seqlens_k = alloc.tables(requests)   # host int32 arrays
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "decode", "kv_append", "decode_num_splits", "decode_workspace_bytes", "validate_tables",
+__all__ = ["prefill", "decode", "kv_append", "SegmentAllocator", "decode_num_splits", "decode_workspace_bytes", "validate_tables",
            "status_string", "version", "library_path", "SegAttnError", "KV_BF16", "KV_FP8_E4M3",
            "KV_INT8"]
 
@@ -71,6 +73,31 @@ def _load():
     lib.seg_attn_validate_tables.restype = I32
     lib.seg_attn_version.argtypes = []
     lib.seg_attn_version.restype = I32
+    PI64 = ctypes.POINTER(I64)
+    lib.seg_attn_allocator_create.argtypes = [I64, I64, ctypes.POINTER(P)]
+    lib.seg_attn_allocator_create.restype = I32
+    lib.seg_attn_allocator_destroy.argtypes = [P]
+    lib.seg_attn_allocator_destroy.restype = None
+    lib.seg_attn_allocator_grow.argtypes = [P, I64, I64]
+    lib.seg_attn_allocator_grow.restype = I32
+    lib.seg_attn_allocator_grow_batch.argtypes = [P, P, P, I32, ctypes.POINTER(I32)]
+    lib.seg_attn_allocator_grow_batch.restype = I32
+    lib.seg_attn_allocator_reserve.argtypes = [P, I64, I64]
+    lib.seg_attn_allocator_reserve.restype = I32
+    lib.seg_attn_allocator_capacity.argtypes = [P, I64]
+    lib.seg_attn_allocator_capacity.restype = I64
+    lib.seg_attn_allocator_release.argtypes = [P, I64]
+    lib.seg_attn_allocator_release.restype = I32
+    lib.seg_attn_allocator_truncate.argtypes = [P, I64, I64]
+    lib.seg_attn_allocator_truncate.restype = I32
+    lib.seg_attn_allocator_length.argtypes = [P, I64]
+    lib.seg_attn_allocator_length.restype = I64
+    lib.seg_attn_allocator_tables.argtypes = [P, P, I32, P, I64, P, P, PI64]
+    lib.seg_attn_allocator_tables.restype = I32
+    lib.seg_attn_allocator_stats.argtypes = [P, PI64, PI64, PI64, PI64]
+    lib.seg_attn_allocator_stats.restype = I32
+    lib.seg_attn_allocator_free_runs.argtypes = [P, P, I64, PI64]
+    lib.seg_attn_allocator_free_runs.restype = I32
     _lib = lib
     return lib
 
@@ -294,6 +321,116 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, segs: torch.Tensor, seg_
                                     _ptr(v_scale if scaled else None), stream)
     if st != 0:
         raise SegAttnError("seg_attn_kv_append", st)
+
+
+class SegmentAllocator:
+    """Host-side segment allocator over a pool of ``pool_tokens`` slots (the
+    seg_attn_allocator_* functions of seg_attn.h). Not thread-safe.
+
+    grow(request, n) adds n keys and raises SegAttnError (status 6), changing nothing, when the
+    request's spare capacity and the free slots hold fewer; shortfalls are rounded up to
+    ``granule`` slots. reserve(request, capacity) sets slots aside for a known final length.
+    tables(requests) returns host int32 numpy arrays (segs [nseg, 2], seg_indptr [B+1],
+    cu_seqlens_k [B+1]) for the entry points; move them to the device with
+    torch.from_numpy(...).to(device)."""
+
+    def __init__(self, pool_tokens: int, granule: int = 1):
+        self._lib = _load()
+        h = ctypes.c_void_p()
+        st = self._lib.seg_attn_allocator_create(int(pool_tokens), int(granule), ctypes.byref(h))
+        if st != 0:
+            raise SegAttnError("seg_attn_allocator_create", st)
+        self._h = h
+        self.pool_tokens = int(pool_tokens)
+        self.granule = int(granule)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value is not None:
+            self._lib.seg_attn_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _call(self, name, *args):
+        if self._h is None:
+            raise RuntimeError("allocator is closed")
+        st = getattr(self._lib, name)(self._h, *args)
+        if st != 0:
+            raise SegAttnError(name, st)
+
+    def grow(self, request: int, n: int) -> None:
+        self._call("seg_attn_allocator_grow", int(request), int(n))
+
+    def grow_many(self, requests, n) -> None:
+        """grow(requests[i], n[i]) in order in one call; on failure raises SegAttnError with the
+        number applied before the failing one in its ``done`` attribute."""
+        import numpy as np
+        req = np.ascontiguousarray(np.asarray(requests, dtype=np.int64).reshape(-1))
+        cnt = np.ascontiguousarray(np.broadcast_to(np.asarray(n, dtype=np.int64), req.shape))
+        done = ctypes.c_int32(0)
+        if self._h is None:
+            raise RuntimeError("allocator is closed")
+        st = self._lib.seg_attn_allocator_grow_batch(self._h, req.ctypes.data, cnt.ctypes.data,
+                                                     req.shape[0], ctypes.byref(done))
+        if st != 0:
+            err = SegAttnError("seg_attn_allocator_grow_batch", st)
+            err.done = int(done.value)
+            raise err
+
+    def reserve(self, request: int, capacity: int) -> None:
+        self._call("seg_attn_allocator_reserve", int(request), int(capacity))
+
+    def release(self, request: int) -> None:
+        self._call("seg_attn_allocator_release", int(request))
+
+    def truncate(self, request: int, new_length: int) -> None:
+        self._call("seg_attn_allocator_truncate", int(request), int(new_length))
+
+    def length(self, request: int) -> int:
+        if self._h is None:
+            raise RuntimeError("allocator is closed")
+        return int(self._lib.seg_attn_allocator_length(self._h, int(request)))
+
+    def capacity(self, request: int) -> int:
+        if self._h is None:
+            raise RuntimeError("allocator is closed")
+        return int(self._lib.seg_attn_allocator_capacity(self._h, int(request)))
+
+    def stats(self) -> dict:
+        v = [ctypes.c_int64(0) for _ in range(4)]
+        self._call("seg_attn_allocator_stats", *[ctypes.byref(x) for x in v])
+        return dict(zip(("free_tokens", "largest_free_run", "free_runs", "requests"),
+                        (int(x.value) for x in v)))
+
+    def free_runs(self):
+        import numpy as np
+        cnt = ctypes.c_int64(0)
+        st = self._lib.seg_attn_allocator_free_runs(self._h, None, 0, ctypes.byref(cnt))
+        if st not in (0, 3):
+            raise SegAttnError("seg_attn_allocator_free_runs", st)
+        runs = np.zeros((max(int(cnt.value), 1), 2), dtype=np.int32)
+        self._call("seg_attn_allocator_free_runs", runs.ctypes.data, runs.shape[0], ctypes.byref(cnt))
+        return runs[:int(cnt.value)]
+
+    def tables(self, requests):
+        import numpy as np
+        req = np.ascontiguousarray(np.asarray(requests, dtype=np.int64).reshape(-1))
+        b = req.shape[0]
+        ind = np.zeros(b + 1, dtype=np.int32)
+        cu = np.zeros(b + 1, dtype=np.int32)
+        n = ctypes.c_int64(0)
+        st = self._lib.seg_attn_allocator_tables(self._h, req.ctypes.data if b else None, b, None, 0,
+                                                 ind.ctypes.data, cu.ctypes.data, ctypes.byref(n))
+        if st not in (0, 3):
+            raise SegAttnError("seg_attn_allocator_tables", st)
+        segs = np.zeros((max(int(n.value), 1), 2), dtype=np.int32)
+        self._call("seg_attn_allocator_tables", req.ctypes.data if b else None, b, segs.ctypes.data,
+                   segs.shape[0], ind.ctypes.data, cu.ctypes.data, ctypes.byref(n))
+        return segs[:int(n.value)], ind, cu
 
 
 def validate_tables(segs, seg_indptr, cu_seqlens_k, pool_tokens: int, *, cu_seqlens_q=None,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsegattn.so")
-SOURCES = ["api.hip", "prefill.hip", "decode.hip", "append.hip"]
+SOURCES = ["api.hip", "prefill.hip", "decode.hip", "append.hip", "allocator.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32 on its own.
@@ -49,7 +49,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([cc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:

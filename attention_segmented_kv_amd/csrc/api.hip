@@ -129,6 +129,7 @@ const char* seg_attn_status_string(seg_attn_status_t status) {
     case SEG_ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
     case SEG_ATTN_ERR_HIP: return "HIP runtime error at launch";
     case SEG_ATTN_ERR_TABLE: return "inconsistent segment / length tables";
+    case SEG_ATTN_ERR_OUT_OF_MEMORY: return "not enough free pool slots (or host memory)";
     default: return "unknown status";
   }
 }

@@ -115,6 +115,54 @@ def measure_append(name, c, fmt, steps, warmup, dev):
             "work_per_step": work, "timing": "graph replays of %d appends" % APPEND_REPS}
 
 
+def measure_allocator(steps: int = 2000):
+    """Host cost of the segment allocator in a decode loop of the bf16 decode workload's shape:
+    128 live requests in a 2^20-slot pool, each arriving with a lognormal prompt (median 1024,
+    64..8192) and an output length U{64..512}, reserving prompt + output on arrival (granule 64
+    for anything beyond). One step grows every live request by one token and writes the batch's
+    tables; a request that has produced its output is released and a new one arrives in its place.
+    Single-threaded host code through the Python binding: no GPU involved."""
+    import numpy as np
+    import attention_segmented_kv_amd as sa
+    rng = np.random.default_rng(1004)
+    a = sa.SegmentAllocator(1 << 20, granule=64)
+    left = {}
+
+    def arrive(r):
+        prompt = int(np.clip(np.rint(1024.0 * np.exp(rng.standard_normal())), 64, 8192))
+        out = int(rng.integers(64, 513))
+        a.reserve(r, prompt + out)
+        a.grow(r, prompt)
+        left[r] = out
+
+    for r in range(128):
+        arrive(r)
+    nxt, arrivals = 128, 0
+    seg_counts = []
+    t0 = time.perf_counter()
+    for step in range(steps):
+        ids = list(left)
+        a.grow_many(ids, 1)
+        segs, ind, cu = a.tables(ids)
+        seg_counts.append(len(segs))
+        for r in ids:
+            left[r] -= 1
+            if left[r] == 0:
+                del left[r]
+                a.release(r)
+                arrive(nxt)
+                nxt += 1
+                arrivals += 1
+    dt = time.perf_counter() - t0
+    st = a.stats()
+    return {"workload": "allocator_decode_loop_b128", "value": round(steps / dt, 1), "unit": "steps/s",
+            "us_per_step": round(dt / steps * 1e6, 2), "bound": "host", "cores": 1,
+            "segments_per_request_mean": round(float(np.mean(seg_counts)) / 128, 3),
+            "arrivals": arrivals, "free_runs": st["free_runs"],
+            "note": "one batched grow of 128 requests by one token + their tables per step, releases "
+                    "and arrivals included, via the Python binding"}
+
+
 def make_step(w):
     import attention_segmented_kv_amd as sa
     import torch
@@ -345,6 +393,10 @@ def main():
             app.append(r)
             torch.cuda.empty_cache()
         result["append"] = app
+        log("[bench] allocator (host)")
+        result["allocator"] = measure_allocator()
+        log(f"[bench] allocator_decode_loop_b128: {result['allocator']['us_per_step']} us per step, "
+            f"{result['allocator']['segments_per_request_mean']} segments per request")
 
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

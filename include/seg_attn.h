@@ -12,7 +12,8 @@
  * results per block and reduces them per request with a log-sum-exp merge (FlashAccel article,
  * "data layout": blockwise partial attention reduced per request; the running max m_i and
  * normaliser l_i of "FlashAttention on Ascend NPU", bottleneck 2). A third writes new tokens
- * into the segments (bf16, or FP8 quantised on write) ahead of either.
+ * into the segments (bf16, or FP8 / INT8 quantised on write) ahead of either, and a host-side
+ * allocator hands out the segments and writes the tables.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -69,7 +70,8 @@ enum {
   SEG_ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim != 128 or Hq/Hkv != 8 */
   SEG_ATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
   SEG_ATTN_ERR_HIP = 4,         /* the HIP runtime reported an error at launch */
-  SEG_ATTN_ERR_TABLE = 5        /* seg_attn_validate_tables found an inconsistent table */
+  SEG_ATTN_ERR_TABLE = 5,       /* seg_attn_validate_tables found an inconsistent table */
+  SEG_ATTN_ERR_OUT_OF_MEMORY = 6 /* the allocator's pool (or the host heap) cannot hold it */
 };
 
 /* KV pool formats. FP8 and INT8 pools hold one-byte codes plus one fp32 scale per (token, kv
@@ -187,6 +189,86 @@ seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
                                      int32_t head_dim, int64_t pool_tokens, int32_t kv_dtype,
                                      void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                                      seg_attn_stream_t stream);
+
+/*
+ * Segment allocator (host only; no GPU call). Hands out ranges of a pool of `pool_tokens` slots
+ * to requests, keeping each request's cache in as few contiguous segments as the free space
+ * allows (Flood README, "Introduction": segmentable blocks instead of paged blocks, for the
+ * continuity of each request's cache), and writes the tables the entry points above take.
+ *
+ * Policy: a request owns slot ranges holding C slots (its capacity), in the order they were
+ * added; its L <= C keys are the first L of them, and the tables list only those. Growing a
+ * request by n keys uses spare capacity first; a shortfall of m slots is allocated aiming at
+ * m rounded up to the allocator's granule (exactly m if that does not fit), so that a request
+ * growing one token at a time gets a new range only every `granule` tokens; reserve sets
+ * capacity aside for a known final length. An allocation first extends the request's last
+ * range over the free slots that directly follow it; the rest goes to the smallest free run
+ * that holds it (lowest start among equals), from the run's start; if no run holds it, the
+ * largest run (lowest start among equals) gives what it has and the rest is placed the same
+ * way. Released and truncated slots merge with neighbouring free runs.
+ *
+ * Requests are named by any int64 id; an id never grown has no keys. The allocator tracks slots
+ * only: moving K/V data is the caller's (seg_attn_kv_append writes new tokens). One allocator
+ * must not be used from two threads at once. A SEG_ATTN_ERR_OUT_OF_MEMORY caused by the pool
+ * (n larger than the free slots) changes nothing; one caused by a failing host allocation
+ * leaves the allocator unusable (destroy it).
+ */
+typedef struct seg_attn_allocator seg_attn_allocator_t;
+
+/* A new allocator over slots [0, pool_tokens), all free; pool_tokens <= INT32_MAX; growth
+ * shortfalls are rounded up to `granule` >= 1 slots (1: exact). */
+seg_attn_status_t seg_attn_allocator_create(int64_t pool_tokens, int64_t granule,
+                                            seg_attn_allocator_t** out);
+void seg_attn_allocator_destroy(seg_attn_allocator_t* allocator);
+
+/* Add n >= 0 keys to `request` (as above). SEG_ATTN_ERR_OUT_OF_MEMORY, with nothing changed,
+ * if its spare capacity and the free slots together hold fewer than n. */
+seg_attn_status_t seg_attn_allocator_grow(seg_attn_allocator_t* allocator, int64_t request,
+                                          int64_t n);
+/* seg_attn_allocator_grow(requests[i], n[i]) for i = 0 .. count-1 in order, stopping at the
+ * first that fails (whose status is returned); *done (if not NULL) receives how many were
+ * applied. One call per decode step instead of one per request. */
+seg_attn_status_t seg_attn_allocator_grow_batch(seg_attn_allocator_t* allocator,
+                                                const int64_t* requests, const int64_t* n,
+                                                int32_t count, int32_t* done);
+/* Make the capacity of `request` at least `capacity` slots without adding keys (a no-op if it is
+ * already); SEG_ATTN_ERR_OUT_OF_MEMORY, with nothing changed, if the free slots do not hold the
+ * difference. */
+seg_attn_status_t seg_attn_allocator_reserve(seg_attn_allocator_t* allocator, int64_t request,
+                                             int64_t capacity);
+/* Free every slot of `request` and forget it (a no-op for an unknown id). */
+seg_attn_status_t seg_attn_allocator_release(seg_attn_allocator_t* allocator, int64_t request);
+/* Keep the first new_length keys of `request` and free every later slot it owns, spare capacity
+ * included (a no-op if it has no more than new_length keys). */
+seg_attn_status_t seg_attn_allocator_truncate(seg_attn_allocator_t* allocator, int64_t request,
+                                              int64_t new_length);
+/* Keys (length) and owned slots (capacity) of `request` (0 if unknown), or -1 for a NULL
+ * allocator. */
+int64_t seg_attn_allocator_length(const seg_attn_allocator_t* allocator, int64_t request);
+int64_t seg_attn_allocator_capacity(const seg_attn_allocator_t* allocator, int64_t request);
+
+/*
+ * HOST tables for the batch requests[0 .. batch): segs [*nseg] (capacity segs_capacity),
+ * seg_indptr [batch+1] and cu_seqlens_k [batch+1], in the layout of the header comment, ready to
+ * be copied to the device. *nseg (if not NULL) receives the number of segments needed; when it
+ * exceeds segs_capacity nothing else is written and SEG_ATTN_ERR_WORKSPACE is returned.
+ */
+seg_attn_status_t seg_attn_allocator_tables(const seg_attn_allocator_t* allocator,
+                                            const int64_t* requests, int32_t batch,
+                                            seg_attn_segment_t* segs, int64_t segs_capacity,
+                                            int32_t* seg_indptr, int32_t* cu_seqlens_k,
+                                            int64_t* nseg);
+
+/* Free slot count, longest free run, number of free runs and of live requests (any may be NULL). */
+seg_attn_status_t seg_attn_allocator_stats(const seg_attn_allocator_t* allocator,
+                                           int64_t* free_tokens, int64_t* largest_free_run,
+                                           int64_t* free_runs, int64_t* requests);
+
+/* The free runs in pool order as (start, length) pairs; *count receives their number, and if
+ * it exceeds capacity nothing else is written and SEG_ATTN_ERR_WORKSPACE is returned. */
+seg_attn_status_t seg_attn_allocator_free_runs(const seg_attn_allocator_t* allocator,
+                                               seg_attn_segment_t* runs, int64_t capacity,
+                                               int64_t* count);
 
 /* Static text for a status code; never NULL. */
 const char* seg_attn_status_string(seg_attn_status_t status);
