@@ -373,3 +373,97 @@ def host_tables(w: Workload):
     """Integer tables as host numpy int64 arrays: segs [nseg, 2], seg_indptr, cu_q, cu_k."""
     f = lambda t: t.detach().cpu().numpy().astype(np.int64)
     return f(w.segs).reshape(-1, 2), f(w.seg_indptr), f(w.cu_seqlens_q), f(w.cu_seqlens_k)
+
+
+# ----------------------------------------------------------------------------------------------
+# segment linear attention (simple gated linear attention over a pool of per-request states)
+
+LA_HEADS, LA_DIM = 16, 128
+
+
+@dataclass
+class LinearWorkload:
+    """Inputs of a segment-linear-attention call.
+
+    q, k, v   [T, H, D] bfloat16; g [T, H] float32 log decays (<= 0)
+    cu_seqlens [B + 1] int32 (decode: 0, 1, ..., B)
+    state_pool [slots, H, D, D] float32, slot state_slots[b] holding request b's state (d_k rows,
+               d_v contiguous); slots no request names are NaN when poisoned
+    state_slots [B] int32, distinct"""
+    name: str
+    kind: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    cu_seqlens: torch.Tensor
+    state_pool: torch.Tensor
+    state_slots: torch.Tensor
+    initial_state: bool
+    scale: float
+    lens: np.ndarray
+    seed: int
+    recipe: str = ""
+
+    @property
+    def batch(self) -> int:
+        return int(self.cu_seqlens.shape[0] - 1)
+
+    @property
+    def num_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    def to(self, device) -> "LinearWorkload":
+        f = lambda t: t.to(device)
+        return LinearWorkload(self.name, self.kind, f(self.q), f(self.k), f(self.v), f(self.g),
+                              f(self.cu_seqlens), f(self.state_pool), f(self.state_slots),
+                              self.initial_state, self.scale, self.lens, self.seed, self.recipe)
+
+
+def make_linear(seed: int, lens: Sequence[int], *, kind: str = "prefill", initial_state: bool = True,
+                num_heads: int = LA_HEADS, head_dim: int = LA_DIM, slack: int = 2,
+                device="cpu", poison: bool = True, name: str = "", recipe: str = "") -> LinearWorkload:
+    """Seeded inputs: q, k, v ~ N(0, 1) rounded to bf16; g = log(sigmoid(z)) / 16 with
+    z ~ N(0, 1) (mean about -0.05: a 64-token chunk keeps a few percent of the state before it);
+    initial states 0.1 * N(0, 1) in ``slack`` times as many slots as requests, at random distinct
+    slots. Values are drawn in the order q, k, v, z, states from one torch generator."""
+    rng = np.random.default_rng(seed)
+    lens_np = np.array([int(x) for x in lens], dtype=np.int64)
+    B = len(lens_np)
+    T = int(lens_np.sum())
+    gen = _new_generator(device, seed)
+    H, D = num_heads, head_dim
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    q = rnd(T, H, D).to(torch.bfloat16)
+    k = rnd(T, H, D).to(torch.bfloat16)
+    v = rnd(T, H, D).to(torch.bfloat16)
+    g = (torch.nn.functional.logsigmoid(rnd(T, H)) / 16.0).to(torch.float32)
+    slots_n = max(1, slack * B)
+    pool = torch.full((slots_n, H, D, D), float("nan") if poison else 0.0, dtype=torch.float32,
+                      device=device)
+    slots = rng.permutation(slots_n)[:B].astype(np.int64)
+    for b in range(B):
+        pool[int(slots[b])] = 0.1 * rnd(H, D, D)
+    cu = _prefix(lens_np)
+    i32 = lambda a: torch.as_tensor(np.asarray(a, dtype=np.int32)).to(device)
+    return LinearWorkload(name or f"linear_{seed}", kind, q, k, v, g, i32(cu), pool, i32(slots),
+                          bool(initial_state), 1.0 / math.sqrt(D), lens_np, seed, recipe)
+
+
+LINEAR_CONFIGS = {
+    "la_prefill_b1_1024": dict(lens=[1024], kind="prefill", initial_state=False),
+    "la_prefill_b2_1024": dict(lens=[1024, 1024], kind="prefill", initial_state=False),
+    "la_decode_b64": dict(lens=[1] * 64, kind="decode", initial_state=True),
+    "la_decode_b256": dict(lens=[1] * 256, kind="decode", initial_state=True),
+}
+
+
+def make_linear_config(name: str, *, device="cpu", poison: bool = True) -> LinearWorkload:
+    """The shapes of the Flood README's Seg-linear-attn table (16 heads, 16 kv heads, head dim
+    128; prefill batch 1 and 2 of 1024 tokens from a zero state, decode batch 64 and 256 from
+    stored states), seeded with 2000 + the table row."""
+    c = LINEAR_CONFIGS[name]
+    seed = 2000 + list(LINEAR_CONFIGS).index(name)
+    return make_linear(seed, c["lens"], kind=c["kind"], initial_state=c["initial_state"],
+                       device=device, poison=poison, name=name,
+                       recipe=f"{c['kind']} B={len(c['lens'])} L={max(c['lens'])}, 16/16 heads, d=128")
