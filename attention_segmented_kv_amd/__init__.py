@@ -22,7 +22,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "decode", "kv_append", "SegmentAllocator", "decode_num_splits", "decode_workspace_bytes", "validate_tables",
+__all__ = ["prefill", "decode", "kv_append", "linear_prefill", "linear_decode", "SegmentAllocator",
+           "decode_num_splits", "decode_workspace_bytes", "validate_tables",
            "status_string", "version", "library_path", "SegAttnError", "KV_BF16", "KV_FP8_E4M3",
            "KV_INT8"]
 
@@ -73,6 +74,10 @@ def _load():
     lib.seg_attn_validate_tables.restype = I32
     lib.seg_attn_version.argtypes = []
     lib.seg_attn_version.restype = I32
+    lib.seg_attn_linear_prefill.argtypes = [P, P, P, P, P, P, I32, I32, I32, F32, I32, P, I64, P, P]
+    lib.seg_attn_linear_prefill.restype = I32
+    lib.seg_attn_linear_decode.argtypes = [P, P, P, P, P, I32, I32, I32, F32, P, I64, P, P]
+    lib.seg_attn_linear_decode.restype = I32
     PI64 = ctypes.POINTER(I64)
     lib.seg_attn_allocator_create.argtypes = [I64, I64, ctypes.POINTER(P)]
     lib.seg_attn_allocator_create.restype = I32
@@ -321,6 +326,82 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, segs: torch.Tensor, seg_
                                     _ptr(v_scale if scaled else None), stream)
     if st != 0:
         raise SegAttnError("seg_attn_kv_append", st)
+
+
+def _check_linear(q, k, v, g, state_slots, state_pool, batch):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a GPU tensor")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, (torch.bfloat16,), dev, 3)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same shape")
+    T, H, D = q.shape
+    _check(g, "g", (torch.float32,), dev, 2)
+    if tuple(g.shape) != (T, H):
+        raise ValueError("g must have shape [T, H]")
+    _check(state_slots, "state_slots", (torch.int32,), dev, 1)
+    if state_slots.shape[0] != batch:
+        raise ValueError("state_slots must have one entry per request")
+    _check(state_pool, "state_pool", (torch.float32,), dev, 4)
+    if tuple(state_pool.shape[1:]) != (H, D, D):
+        raise ValueError("state_pool must have shape [slots, H, D, D]")
+    return dev, T, H, D
+
+
+def linear_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                   cu_seqlens: torch.Tensor, state_slots: torch.Tensor, state_pool: torch.Tensor, *,
+                   initial_state: bool = True, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Segment linear attention over a varlen batch; see seg_attn_linear_prefill. The final
+    states are written to state_pool[state_slots] in place. Returns out [T, H, 128] bf16."""
+    lib = _load()
+    batch = cu_seqlens.shape[0] - 1
+    dev, T, H, D = _check_linear(q, k, v, g, state_slots, state_pool, batch)
+    _check(cu_seqlens, "cu_seqlens", (torch.int32,), dev, 1)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", (torch.bfloat16,), dev, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.seg_attn_linear_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(cu_seqlens),
+                                         _ptr(state_slots), batch, H, D, float(scale),
+                                         1 if initial_state else 0, _ptr(state_pool),
+                                         state_pool.shape[0], _ptr(out), stream)
+    if st != 0:
+        raise SegAttnError("seg_attn_linear_prefill", st)
+    return out
+
+
+def linear_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  state_slots: torch.Tensor, state_pool: torch.Tensor, *, scale: Optional[float] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per request (row b of q, k, v, g) against its state slot, updated in place; see
+    seg_attn_linear_decode. Returns out [B, H, 128] bf16."""
+    lib = _load()
+    batch = q.shape[0]
+    dev, T, H, D = _check_linear(q, k, v, g, state_slots, state_pool, batch)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", (torch.bfloat16,), dev, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.seg_attn_linear_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state_slots), batch,
+                                        H, D, float(scale), _ptr(state_pool), state_pool.shape[0],
+                                        _ptr(out), stream)
+    if st != 0:
+        raise SegAttnError("seg_attn_linear_decode", st)
+    return out
 
 
 class SegmentAllocator:

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsegattn.so")
-SOURCES = ["api.hip", "prefill.hip", "decode.hip", "append.hip", "allocator.cpp"]
+SOURCES = ["api.hip", "prefill.hip", "decode.hip", "append.hip", "linear.hip", "allocator.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32 on its own.

@@ -26,6 +26,13 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const void* se
                             int batch, int total_new, int hkv, int64_t pool_tokens, int fmt,
                             void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                             hipStream_t stream);
+hipError_t launch_linear_prefill(const void* q, const void* k, const void* v, const float* g,
+                                 const int32_t* cu, const int32_t* slots, int batch, int heads,
+                                 float scale, int initial_state, float* pool, int64_t pool_slots,
+                                 void* out, hipStream_t stream);
+hipError_t launch_linear_decode(const void* q, const void* k, const void* v, const float* g,
+                                const int32_t* slots, int batch, int heads, float scale, float* pool,
+                                int64_t pool_slots, void* out, hipStream_t stream);
 }  // namespace segattn
 
 namespace {
@@ -261,6 +268,63 @@ seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
                                              cu_seqlens_k, batch, total_new, num_heads_kv,
                                              pool_tokens, kv_dtype, k_pool, v_pool, k_scale,
                                              v_scale, (hipStream_t)stream);
+    return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
+  } catch (...) {
+    return SEG_ATTN_ERR_HIP;
+  }
+}
+
+namespace {
+// Shared argument checks of the two linear-attention entry points.
+seg_attn_status_t check_linear(const void* q, const void* k, const void* v, const float* g,
+                               const int32_t* slots, int32_t batch, int32_t heads, int32_t head_dim,
+                               float scale, const float* pool, int64_t pool_slots, const void* out) {
+  if (batch < 0 || heads <= 0 || head_dim <= 0 || pool_slots < 0) return SEG_ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return SEG_ATTN_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim) return SEG_ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)batch * heads * 2 > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
+  if (batch == 0) return SEG_ATTN_OK;
+  if (!q || !k || !v || !g || !slots || !pool || !out) return SEG_ATTN_ERR_INVALID_ARG;
+  auto misaligned = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(pool, 16) ||
+      misaligned(out, 8) || misaligned(g, 4))
+    return SEG_ATTN_ERR_INVALID_ARG;
+  return SEG_ATTN_OK;
+}
+}  // namespace
+
+seg_attn_status_t seg_attn_linear_prefill(const void* q, const void* k, const void* v,
+                                          const float* g, const int32_t* cu_seqlens,
+                                          const int32_t* state_slots, int32_t batch,
+                                          int32_t num_heads, int32_t head_dim, float scale,
+                                          int32_t initial_state, float* state_pool,
+                                          int64_t pool_slots, void* out, seg_attn_stream_t stream) {
+  try {
+    if (initial_state != 0 && initial_state != 1) return SEG_ATTN_ERR_INVALID_ARG;
+    seg_attn_status_t st = check_linear(q, k, v, g, state_slots, batch, num_heads, head_dim, scale,
+                                        state_pool, pool_slots, out);
+    if (st != SEG_ATTN_OK || batch == 0) return st;
+    if (!cu_seqlens) return SEG_ATTN_ERR_INVALID_ARG;
+    hipError_t e = segattn::launch_linear_prefill(q, k, v, g, cu_seqlens, state_slots, batch, num_heads,
+                                                  scale, initial_state, state_pool, pool_slots, out,
+                                                  (hipStream_t)stream);
+    return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
+  } catch (...) {
+    return SEG_ATTN_ERR_HIP;
+  }
+}
+
+seg_attn_status_t seg_attn_linear_decode(const void* q, const void* k, const void* v, const float* g,
+                                         const int32_t* state_slots, int32_t batch,
+                                         int32_t num_heads, int32_t head_dim, float scale,
+                                         float* state_pool, int64_t pool_slots, void* out,
+                                         seg_attn_stream_t stream) {
+  try {
+    seg_attn_status_t st = check_linear(q, k, v, g, state_slots, batch, num_heads, head_dim, scale,
+                                        state_pool, pool_slots, out);
+    if (st != SEG_ATTN_OK || batch == 0) return st;
+    hipError_t e = segattn::launch_linear_decode(q, k, v, g, state_slots, batch, num_heads, scale,
+                                                 state_pool, pool_slots, out, (hipStream_t)stream);
     return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
   } catch (...) {
     return SEG_ATTN_ERR_HIP;

@@ -30,7 +30,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = {"prefill": "attention_segmented_kv_amd/csrc/prefill.hip",
                   "decode": "attention_segmented_kv_amd/csrc/decode.hip",
-                  "append": "attention_segmented_kv_amd/csrc/append.hip"}
+                  "append": "attention_segmented_kv_amd/csrc/append.hip",
+                  "linear": "attention_segmented_kv_amd/csrc/linear.hip"}
 
 
 def log(*a):
@@ -113,6 +114,56 @@ def measure_append(name, c, fmt, steps, warmup, dev):
             "value": round(work / (t["ms_per_step"] * 1e-3) / 1e9, 3), "unit": "GB/s",
             "launch_us_mean": round(t["launch_ms_mean"] * 1e3, 2), "roofline": rf,
             "work_per_step": work, "timing": "graph replays of %d appends" % APPEND_REPS}
+
+
+LINEAR_CASES = ("la_prefill_b1_1024", "la_prefill_b2_1024", "la_decode_b64", "la_decode_b256")
+
+
+def linear_work(w):
+    """Algorithmic work of a segment-linear-attention call. Prefill: the flops of the 64-token
+    chunked form, 2 * 64 * 128 * (128 + 64 + 64 + 128) per chunk and head (Q S, Q K^T, P V,
+    K~^T V; masked work counted, as the chunk computes it). Decode: HBM bytes, the fp32 state
+    read and written (2 * 64 KiB) plus q, k, v, out (4 * 256 B) and g per request and head."""
+    H = w.num_heads
+    if w.kind == "prefill":
+        chunks = int(sum((int(n) + 63) // 64 for n in w.lens))
+        return 2.0 * 64 * 128 * (128 + 64 + 64 + 128) * chunks * H
+    return float(w.batch * H * (2 * 128 * 128 * 4 + 4 * 256 + 4))
+
+
+def measure_linear(name, steps, warmup, dev):
+    import torch
+    import attention_segmented_kv_amd as sa
+    import workloads as wl
+    w = wl.make_linear_config(name, device=dev, poison=False)
+    out = torch.empty_like(w.q)
+
+    def call():
+        if w.kind == "decode":
+            sa.linear_decode(w.q, w.k, w.v, w.g, w.state_slots, w.state_pool, scale=w.scale, out=out)
+        else:
+            sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool,
+                              initial_state=w.initial_state, scale=w.scale, out=out)
+
+    def step():  # graph replays of APPEND_REPS calls, as for the appends
+        for _ in range(APPEND_REPS):
+            call()
+    t = time_steps(step, steps, warmup, graph=True)
+    us = t["launch_ms_mean"] * 1e3 / APPEND_REPS
+    work = linear_work(w)
+    if w.kind == "prefill":
+        achieved = work / (us * 1e-6) / 1e12
+        rf = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+              "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic("linear", name),
+              "note": "latency-bound in practice: one workgroup per (request, head, 64-column half) "
+                      "walks the request's chunks in order"}
+    else:
+        achieved = work / (us * 1e-6) / 1e9
+        rf = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+              "frac": achieved / PEAK_HBM_GBS, "traffic": load_traffic("linear", name)}
+    return {"workload": name, "recipe": w.recipe, "value": round(us, 2), "unit": "us",
+            "higher_is_better": False, "roofline": rf, "work_per_call": work,
+            "timing": "graph replays of %d calls" % APPEND_REPS}
 
 
 def measure_allocator(steps: int = 2000):
@@ -296,6 +347,8 @@ def main():
                     help="time replays of a HIP graph capturing one step instead of eager calls")
     ap.add_argument("--append-only", default=None, metavar="NAME|all",
                     help="only time the KV appends (one named case, or all), one line each on stderr")
+    ap.add_argument("--linear-only", default=None, metavar="NAME|all",
+                    help="only time segment linear attention (one named case, or all)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB, 5 times (reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -335,6 +388,21 @@ def main():
             res.append(r)
             torch.cuda.empty_cache()
         print(json.dumps({"append": res}), flush=True)
+        return
+
+    if args.linear_only:
+        res = []
+        for name in LINEAR_CASES:
+            if args.linear_only not in ("all", name):
+                continue
+            log(f"[bench] timing {name}: warmup {args.warmup}, steps {args.steps}")
+            r = measure_linear(name, args.steps, args.warmup, dev)
+            rf = r["roofline"]
+            log(f"[bench] {name}: {r['value']:.2f} us per call, {rf['achieved']:.1f} {rf['unit']}, "
+                f"roofline frac {rf['frac']:.3f}")
+            res.append(r)
+            torch.cuda.empty_cache()
+        print(json.dumps({"linear": res}), flush=True)
         return
 
     head_c = args.config
@@ -393,6 +461,15 @@ def main():
             app.append(r)
             torch.cuda.empty_cache()
         result["append"] = app
+        lin = []
+        for name in LINEAR_CASES:
+            log(f"[bench] {name}: generating")
+            r = measure_linear(name, max(20, args.steps // 2), args.warmup, dev)
+            rf = r["roofline"]
+            log(f"[bench] {name}: {r['value']:.2f} us, {rf['achieved']:.1f} {rf['unit']}, frac {rf['frac']:.3f}")
+            lin.append(r)
+            torch.cuda.empty_cache()
+        result["linear"] = lin
         log("[bench] allocator (host)")
         result["allocator"] = measure_allocator()
         log(f"[bench] allocator_decode_loop_b128: {result['allocator']['us_per_step']} us per step, "

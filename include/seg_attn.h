@@ -191,6 +191,36 @@ seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
                                      seg_attn_stream_t stream);
 
 /*
+ * Segment linear attention: simple gated linear attention over a pool of per-request states, the
+ * kernel family of the Flood README's "Seg-linear-attn" table (16 heads, 16 kv heads, head dim
+ * 128, against flash-linear-attention's chunked and recurrent simple GLA). Per request and head,
+ * with a log decay g_t <= 0 per token and head:
+ *   S_t = exp(g_t) S_{t-1} + k_t^T v_t,   o_t = scale * q_t S_t   (S: 128 x 128)
+ * q, k, v      [T, H, 128] bf16 (query and kv heads are equal in number); g [T, H] fp32.
+ * state_pool   [pool_slots, H, 128, 128] fp32: request b's state is slot state_slots[b] (rows
+ *              are d_k, the 128 d_v values of a row contiguous). Slots must be distinct within a
+ *              call; a slot outside [0, pool_slots) makes its request a no-op.
+ * out          [T, H, 128] bf16.
+ * Prefill: request b's tokens are rows cu_seqlens[b] .. cu_seqlens[b+1]-1; its state starts
+ * from its slot (initial_state = 1) or from zero (0) and the final state is written back to the
+ * slot. Chunks of 64 tokens; the products run on bf16 operands with fp32 accumulation and an
+ * fp32 state. Decode: one token per request (row b), state read from and written to the slot,
+ * in fp32 throughout. Buffers: q, k, v and the pool 16-byte aligned, out 8-byte.
+ * Returns SEG_ATTN_OK, or an error before anything is launched.
+ */
+seg_attn_status_t seg_attn_linear_prefill(const void* q, const void* k, const void* v,
+                                          const float* g, const int32_t* cu_seqlens,
+                                          const int32_t* state_slots, int32_t batch,
+                                          int32_t num_heads, int32_t head_dim, float scale,
+                                          int32_t initial_state, float* state_pool,
+                                          int64_t pool_slots, void* out, seg_attn_stream_t stream);
+seg_attn_status_t seg_attn_linear_decode(const void* q, const void* k, const void* v, const float* g,
+                                         const int32_t* state_slots, int32_t batch,
+                                         int32_t num_heads, int32_t head_dim, float scale,
+                                         float* state_pool, int64_t pool_slots, void* out,
+                                         seg_attn_stream_t stream);
+
+/*
  * Segment allocator (host only; no GPU call). Hands out ranges of a pool of `pool_tokens` slots
  * to requests, keeping each request's cache in as few contiguous segments as the free space
  * allows (Flood README, "Introduction": segmentable blocks instead of paged blocks, for the

@@ -119,6 +119,36 @@ def test_kv_append_without_new_tokens_is_a_noop():
     assert lib.seg_attn_kv_append(*_append_args(batch=0, tn=0)) == 0
 
 
+def _linear_args(**over):
+    a = dict(q=256, k=256, v=256, g=256, cu=1, slots=1, batch=2, h=16, d=128, scale=0.1, init=1,
+             pool=256, npool=4, out=256, stream=None)
+    a.update(over)
+    return [a[k] for k in ("q", "k", "v", "g", "cu", "slots", "batch", "h", "d", "scale", "init",
+                           "pool", "npool", "out", "stream")]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(pool=None), 1), (dict(cu=None), 1), (dict(batch=-1), 1), (dict(h=0), 1),
+    (dict(d=64), 2), (dict(init=2), 1), (dict(scale=float("inf")), 1), (dict(npool=-1), 1),
+    (dict(k=264), 1), (dict(out=260), 1), (dict(batch=0), 0),
+])
+def test_linear_prefill_rejects_bad_arguments(over, status):
+    lib = _lib()
+    assert lib.seg_attn_linear_prefill(*_linear_args(**over)) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(slots=None), 1), (dict(d=96), 2), (dict(h=-3), 1), (dict(v=8), 1),
+    (dict(batch=0, q=None), 0),
+])
+def test_linear_decode_rejects_bad_arguments(over, status):
+    lib = _lib()
+    a = _linear_args(**over)
+    del a[10]  # no initial_state
+    del a[4]   # no cu_seqlens
+    assert lib.seg_attn_linear_decode(*a) == status
+
+
 def test_split_plan_and_workspace_size():
     _lib()
     n, ln = sa.decode_num_splits(4, 1000, 8, sa.KV_BF16, 4)

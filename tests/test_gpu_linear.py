@@ -1,0 +1,151 @@
+"""GPU parity of segment linear attention (seg_attn_linear_prefill / _decode through the binding)
+against the float64 recurrence of the oracle, outputs and final states.
+
+Linear-attention outputs are unnormalised decayed sums (|o| reaches 20 on these inputs), so the
+bar is relative to the reference's size: RMS error <= 5e-3 of the reference's RMS and max error
+<= 1e-2 of its largest magnitude for outputs, 5e-3 of the largest magnitude for states. A CPU
+emulation of the kernel's roundings (bf16 output, bf16 P, K~ and state operand, fp32 state)
+gives 2.4e-3, 4e-3 and 2e-3 on the full-size inputs; the bars leave a factor of two.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+REL_RMS, REL_MAX, STATE_REL = 5e-3, 1e-2, 5e-3
+
+
+def _sa():
+    import attention_segmented_kv_amd as sa
+    return sa
+
+
+def _assert_rel(got, ref, name, rms_tol=REL_RMS, max_tol=REL_MAX):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{name}: non-finite output"
+    err = np.abs(got - ref)
+    scale_rms = max(np.sqrt((ref ** 2).mean()), 1e-30)
+    scale_max = max(np.abs(ref).max(), 1e-30)
+    rel_rms = np.sqrt((err ** 2).mean()) / scale_rms
+    rel_max = err.max() / scale_max
+    print(f"[parity] {name}: rel_rms={rel_rms:.2e} rel_max={rel_max:.2e}", flush=True)
+    assert rel_rms <= rms_tol and rel_max <= max_tol, f"{name}: rel_rms {rel_rms:.3e} rel_max {rel_max:.3e}"
+
+
+def _oracle(w, pool_before):
+    s0 = pool_before[w.state_slots.long().cpu()].double().numpy() if w.initial_state else None
+    return oracle.linear_attention(wl.bits(w.q), wl.bits(w.k), wl.bits(w.v), w.g.cpu().numpy(),
+                                   w.cu_seqlens.cpu().numpy(), s0, w.scale)
+
+
+def _run(w):
+    sa = _sa()
+    if w.kind == "decode":
+        return sa.linear_decode(w.q, w.k, w.v, w.g, w.state_slots, w.state_pool, scale=w.scale)
+    return sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool,
+                             initial_state=w.initial_state, scale=w.scale)
+
+
+def _check(w, name):
+    pool_before = w.state_pool.detach().cpu().clone()
+    o_ref, st_ref = _oracle(w, pool_before)
+    out = _run(w)
+    torch.cuda.synchronize()
+    _assert_rel(out.float().cpu().numpy(), o_ref, name)
+    pool_after = w.state_pool.detach().cpu()
+    slots = w.state_slots.long().cpu()
+    st = pool_after[slots].double().numpy()
+    srel = np.abs(st - st_ref).max() / max(np.abs(st_ref).max(), 1e-30)
+    print(f"[parity] {name} states: rel_max={srel:.2e}", flush=True)
+    assert srel <= STATE_REL, f"{name}: state rel_max {srel:.3e}"
+    # slots no request names are untouched (bitwise, NaN poison included)
+    keep = torch.ones(pool_after.shape[0], dtype=torch.bool)
+    keep[slots] = False
+    assert torch.equal(pool_after[keep].view(torch.int32), pool_before[keep].view(torch.int32))
+
+
+@needs_gpu
+@pytest.mark.parametrize("initial_state", [False, True])
+def test_linear_prefill_ragged(initial_state):
+    """Lengths around the 64-token chunk: 1, 63, 64, 65, 130, an empty request."""
+    print(f"[case] linear prefill ragged initial_state={initial_state}", flush=True)
+    w = wl.make_linear(31, [1, 63, 64, 65, 130, 0], kind="prefill", initial_state=initial_state,
+                       num_heads=4).to("cuda")
+    _check(w, f"la-ragged-{int(initial_state)}")
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", ["la_prefill_b1_1024", "la_prefill_b2_1024", "la_decode_b64",
+                                  "la_decode_b256"])
+def test_linear_named_workloads(name):
+    print(f"[case] linear {name}", flush=True)
+    w = wl.make_linear_config(name, device="cuda")
+    _check(w, name)
+
+
+@needs_gpu
+def test_linear_decode_small_heads():
+    print("[case] linear decode H=3", flush=True)
+    w = wl.make_linear(32, [1] * 9, kind="decode", num_heads=3).to("cuda")
+    _check(w, "la-decode-h3")
+
+
+@needs_gpu
+def test_linear_prefill_in_pieces_equals_prefill_at_once():
+    """150 tokens at once against 100 then 50 with the state carried through the slot."""
+    sa = _sa()
+    print("[case] linear prefill in pieces", flush=True)
+    w = wl.make_linear(33, [150], kind="prefill", initial_state=True, num_heads=2).to("cuda")
+    pool0 = w.state_pool.clone()
+    full = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool)
+    st_full = w.state_pool[w.state_slots.long()].clone()
+    w.state_pool.copy_(pool0)
+    cu1 = torch.tensor([0, 100], dtype=torch.int32, device="cuda")
+    cu2 = torch.tensor([0, 50], dtype=torch.int32, device="cuda")
+    a = sa.linear_prefill(w.q[:100].contiguous(), w.k[:100].contiguous(), w.v[:100].contiguous(),
+                          w.g[:100].contiguous(), cu1, w.state_slots, w.state_pool)
+    b = sa.linear_prefill(w.q[100:].contiguous(), w.k[100:].contiguous(), w.v[100:].contiguous(),
+                          w.g[100:].contiguous(), cu2, w.state_slots, w.state_pool)
+    torch.cuda.synchronize()
+    ref = full.float().cpu().numpy()
+    _assert_rel(torch.cat([a, b]).float().cpu().numpy(), ref, "la-pieces")
+    st = w.state_pool[w.state_slots.long()].double().cpu().numpy()
+    assert np.abs(st - st_full.double().cpu().numpy()).max() <= STATE_REL * np.abs(st).max()
+
+
+@needs_gpu
+def test_linear_decode_equals_one_token_prefill():
+    sa = _sa()
+    print("[case] linear decode vs one-token prefill", flush=True)
+    w = wl.make_linear(34, [1] * 12, kind="decode", num_heads=4).to("cuda")
+    pool0 = w.state_pool.clone()
+    od = sa.linear_decode(w.q, w.k, w.v, w.g, w.state_slots, w.state_pool)
+    sd = w.state_pool.clone()
+    w.state_pool.copy_(pool0)
+    op = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool)
+    torch.cuda.synchronize()
+    _assert_rel(op.float().cpu().numpy(), od.float().cpu().numpy().astype(np.float64), "la-decode-vs-prefill")
+    sl = w.state_slots.long()
+    a, b = sd[sl].double().cpu().numpy(), w.state_pool[sl].double().cpu().numpy()
+    assert np.abs(a - b).max() <= STATE_REL * np.abs(a).max()
+
+
+@needs_gpu
+def test_linear_prefill_is_deterministic():
+    sa = _sa()
+    print("[case] linear prefill determinism", flush=True)
+    w = wl.make_linear(35, [300, 77], kind="prefill", num_heads=4).to("cuda")
+    pool0 = w.state_pool.clone()
+    o1 = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool)
+    p1 = w.state_pool.clone()
+    w.state_pool.copy_(pool0)
+    o2 = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(p1.view(torch.int32), w.state_pool.view(torch.int32))
