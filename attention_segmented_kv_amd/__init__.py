@@ -74,7 +74,10 @@ def _load():
     lib.seg_attn_validate_tables.restype = I32
     lib.seg_attn_version.argtypes = []
     lib.seg_attn_version.restype = I32
-    lib.seg_attn_linear_prefill.argtypes = [P, P, P, P, P, P, I32, I32, I32, F32, I32, P, I64, P, P]
+    lib.seg_attn_linear_prefill.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, F32, I32, P, I64, P, P,
+                                            SZ, P]
+    lib.seg_attn_linear_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.seg_attn_linear_prefill_workspace_bytes.restype = SZ
     lib.seg_attn_linear_prefill.restype = I32
     lib.seg_attn_linear_decode.argtypes = [P, P, P, P, P, I32, I32, I32, F32, P, I64, P, P]
     lib.seg_attn_linear_decode.restype = I32
@@ -352,9 +355,14 @@ def _check_linear(q, k, v, g, state_slots, state_pool, batch):
 def linear_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                    cu_seqlens: torch.Tensor, state_slots: torch.Tensor, state_pool: torch.Tensor, *,
                    initial_state: bool = True, scale: Optional[float] = None,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   out: Optional[torch.Tensor] = None, max_seqlen: Optional[int] = None,
+                   parallel: bool = True, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Segment linear attention over a varlen batch; see seg_attn_linear_prefill. The final
-    states are written to state_pool[state_slots] in place. Returns out [T, H, 128] bf16."""
+    states are written to state_pool[state_slots] in place. Returns out [T, H, 128] bf16.
+
+    parallel=True runs all chunks in parallel with a workspace (allocated here unless given;
+    max_seqlen is read from cu_seqlens, a device-to-host copy, unless given); parallel=False
+    walks each request's chunks in order in one kernel."""
     lib = _load()
     batch = cu_seqlens.shape[0] - 1
     dev, T, H, D = _check_linear(q, k, v, g, state_slots, state_pool, batch)
@@ -367,12 +375,23 @@ def linear_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
         _check(out, "out", (torch.bfloat16,), dev, 3)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
+    ws_bytes = 0
+    if parallel:
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if batch > 0 else 0
+        need = int(lib.seg_attn_linear_prefill_workspace_bytes(batch, int(max_seqlen), H, D))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        workspace = None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.seg_attn_linear_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(cu_seqlens),
-                                         _ptr(state_slots), batch, H, D, float(scale),
-                                         1 if initial_state else 0, _ptr(state_pool),
-                                         state_pool.shape[0], _ptr(out), stream)
+                                         _ptr(state_slots), batch, int(max_seqlen or 0), H, D,
+                                         float(scale), 1 if initial_state else 0, _ptr(state_pool),
+                                         state_pool.shape[0], _ptr(out), _ptr(workspace), ws_bytes,
+                                         stream)
     if st != 0:
         raise SegAttnError("seg_attn_linear_prefill", st)
     return out

@@ -33,6 +33,11 @@ hipError_t launch_linear_prefill(const void* q, const void* k, const void* v, co
 hipError_t launch_linear_decode(const void* q, const void* k, const void* v, const float* g,
                                 const int32_t* slots, int batch, int heads, float scale, float* pool,
                                 int64_t pool_slots, void* out, hipStream_t stream);
+size_t linear_prefill_ws(int64_t batch, int64_t maxc, int64_t heads, size_t* off);
+hipError_t launch_linear_prefill_parallel(const void* q, const void* k, const void* v, const float* g,
+                                          const int32_t* cu, const int32_t* slots, int batch, int heads,
+                                          int maxc, float scale, int initial_state, float* pool,
+                                          int64_t pool_slots, void* out, void* ws, hipStream_t stream);
 }  // namespace segattn
 
 namespace {
@@ -293,21 +298,40 @@ seg_attn_status_t check_linear(const void* q, const void* k, const void* v, cons
 }
 }  // namespace
 
+size_t seg_attn_linear_prefill_workspace_bytes(int32_t batch, int32_t max_seqlen, int32_t num_heads,
+                                               int32_t head_dim) {
+  if (batch < 0 || max_seqlen < 0 || num_heads <= 0 || head_dim != kHeadDim) return 0;
+  return segattn::linear_prefill_ws(batch, ((int64_t)max_seqlen + 63) / 64, num_heads, nullptr);
+}
+
 seg_attn_status_t seg_attn_linear_prefill(const void* q, const void* k, const void* v,
                                           const float* g, const int32_t* cu_seqlens,
                                           const int32_t* state_slots, int32_t batch,
-                                          int32_t num_heads, int32_t head_dim, float scale,
-                                          int32_t initial_state, float* state_pool,
-                                          int64_t pool_slots, void* out, seg_attn_stream_t stream) {
+                                          int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+                                          float scale, int32_t initial_state, float* state_pool,
+                                          int64_t pool_slots, void* out, void* workspace,
+                                          size_t workspace_bytes, seg_attn_stream_t stream) {
   try {
     if (initial_state != 0 && initial_state != 1) return SEG_ATTN_ERR_INVALID_ARG;
+    if (max_seqlen < 0) return SEG_ATTN_ERR_INVALID_ARG;
     seg_attn_status_t st = check_linear(q, k, v, g, state_slots, batch, num_heads, head_dim, scale,
                                         state_pool, pool_slots, out);
     if (st != SEG_ATTN_OK || batch == 0) return st;
     if (!cu_seqlens) return SEG_ATTN_ERR_INVALID_ARG;
-    hipError_t e = segattn::launch_linear_prefill(q, k, v, g, cu_seqlens, state_slots, batch, num_heads,
-                                                  scale, initial_state, state_pool, pool_slots, out,
-                                                  (hipStream_t)stream);
+    hipError_t e;
+    if (workspace == nullptr) {
+      e = segattn::launch_linear_prefill(q, k, v, g, cu_seqlens, state_slots, batch, num_heads, scale,
+                                         initial_state, state_pool, pool_slots, out, (hipStream_t)stream);
+    } else {
+      const int64_t maxc = ((int64_t)max_seqlen + 63) / 64;
+      if ((int64_t)batch * maxc * num_heads * 2 > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
+      if (((uintptr_t)workspace & 255) != 0) return SEG_ATTN_ERR_INVALID_ARG;
+      if (workspace_bytes < segattn::linear_prefill_ws(batch, maxc, num_heads, nullptr))
+        return SEG_ATTN_ERR_WORKSPACE;
+      e = segattn::launch_linear_prefill_parallel(q, k, v, g, cu_seqlens, state_slots, batch, num_heads,
+                                                  (int)maxc, scale, initial_state, state_pool, pool_slots,
+                                                  out, workspace, (hipStream_t)stream);
+    }
     return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
   } catch (...) {
     return SEG_ATTN_ERR_HIP;

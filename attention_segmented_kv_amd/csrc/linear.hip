@@ -323,6 +323,284 @@ __global__ __launch_bounds__(kLaThreads) void la_prefill_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------- chunk-parallel prefill
+//
+// The sequential kernel walks a request's chunks in order, so B = 1 keeps 32 workgroups busy.
+// With a workspace the same arithmetic runs in three launches over (request, chunk) pairs:
+//   1. every chunk's own state contribution dS^T = V^T K~ (fp32) and its decay sum G_last;
+//   2. a scan per (request, head, 32 d_v columns): S_before(c) written as bf16 S^T, then
+//      S <- exp(G_last(c)) S + dS(c); the final state goes back to the slot;
+//   3. every chunk's outputs, O^T = exp(G) S_before^T Q^T + V^T P^T.
+// Workspace: dS^T [B][maxc][H][128 d][128 i] fp32, S_before^T [B][maxc][H][128 d][128 i] bf16,
+// G_last [B][maxc][H] fp32.
+
+// Stage a chunk's K rows (row-major, swizzled) / K~^T / V^T half and return G for lane t.
+struct ChunkIn {
+  u32x4 rq[4], rk[4], rv[2];
+  float rg;
+};
+
+__device__ __forceinline__ void load_chunk(ChunkIn& in, const uint16_t* q, const uint16_t* k,
+                                           const uint16_t* v, const float* g, int t_begin, int n,
+                                           int c0, int h, int H, int vs, bool want_q) {
+  const int tid = threadIdx.x, lane = tid & 63, srow = tid >> 2;
+  const int t = c0 + srow;
+  const bool ok = t < n;
+  const int64_t hstride = (int64_t)H * kLaDim;
+  const int64_t base = (int64_t)(t_begin + t) * hstride + (int64_t)h * kLaDim;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int ch = 4 * (tid & 3) + c;
+    in.rq[c] = (ok && want_q) ? *reinterpret_cast<const u32x4*>(q + base + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+    in.rk[c] = ok ? *reinterpret_cast<const u32x4*>(k + base + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = 2 * (tid & 3) + c;
+    in.rv[c] = ok ? *reinterpret_cast<const u32x4*>(v + base + 64 * vs + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const int tg = c0 + lane;
+  in.rg = tg < n ? g[(int64_t)(t_begin + tg) * H + h] : 0.f;
+}
+
+// Writes V^T (always), K~^T (with_kt) and Qs/Ks (with_qk) of the staged chunk into LDS.
+__device__ __forceinline__ void stage_chunk(const ChunkIn& in, lds_char_t* lds, float G, float Glast,
+                                            bool with_kt, bool with_qk) {
+  const int tid = threadIdx.x, srow = tid >> 2;
+  if (with_qk) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ch = 4 * (tid & 3) + c;
+      *(__attribute__((address_space(3))) u32x4*)(lds + kQsOff + chunk16(srow, ch)) = in.rq[c];
+      *(__attribute__((address_space(3))) u32x4*)(lds + kKsOff + chunk16(srow, ch)) = in.rk[c];
+    }
+  }
+  if (with_kt) {
+    const float ws = __expf(Glast - __shfl(G, srow, 64));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ch = 4 * (tid & 3) + c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (in.rk[c][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const int i = 8 * ch + e;
+        *(__attribute__((address_space(3))) uint16_t*)(lds + kKtOff + unit8(i, srow >> 2) + 2 * (srow & 3)) =
+            (uint16_t)float_to_bf16_bits(bf16_bits_to_float(bits) * ws);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = 2 * (tid & 3) + c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * ch + e;
+      *(__attribute__((address_space(3))) uint16_t*)(lds + kVtOff + unit8(d, srow >> 2) + 2 * (srow & 3)) =
+          (uint16_t)((in.rv[c][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+  }
+}
+
+// V^T fragments (A operands) of d tile md, s = 16 stp + {4hh..4hh+3, 8+4hh..8+4hh+3}
+__device__ __forceinline__ void read_vt_frags(const lds_char_t* lds, int md, bf16x8 (&vt)[4]) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int stp = 0; stp < 4; ++stp) {
+    const int r = 32 * md + l32;
+    const u32x2 lo = *(const __attribute__((address_space(3))) u32x2*)(lds + kVtOff + unit8(r, 4 * stp + hh));
+    const u32x2 hi = *(const __attribute__((address_space(3))) u32x2*)(lds + kVtOff + unit8(r, 4 * stp + 2 + hh));
+    const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+    vt[stp] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+__global__ __launch_bounds__(kLaThreads) void la_chunk_state_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ g,
+    const int32_t* __restrict__ cu, int H, int maxc, float* __restrict__ ds, float* __restrict__ glast) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kLaLds];
+  lds_char_t* lds = (lds_char_t*)lds_raw;
+  const int vs = blockIdx.x & 1;
+  const int rest = blockIdx.x >> 1;
+  const int h = rest % H;
+  const int bc = rest / H;  // b * maxc + c
+  const int b = bc / maxc, c = bc - b * maxc;
+  const int t_begin = cu[b], n = cu[b + 1] - t_begin;
+  const int c0 = c * kChunk;
+  if (c0 >= n) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int md = wave & 1, np = wave >> 1;
+  ChunkIn in;
+  load_chunk(in, k, k, v, g, t_begin, n, c0, h, H, vs, false);
+  const float G = wave_inclusive_sum(in.rg);
+  const float Glast = __shfl(G, 63, 64);
+  stage_chunk(in, lds, G, Glast, true, false);
+  __syncthreads();
+  bf16x8 vt[4];
+  read_vt_frags(lds, md, vt);
+  float* out = ds + ((int64_t)bc * H + h) * (kLaDim * kLaDim);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = 32 * (2 * np + u) + l32;
+    f32x16 acc = {};
+#pragma unroll
+    for (int stp = 0; stp < 4; ++stp) {
+      const u32x2 lo = *(const __attribute__((address_space(3))) u32x2*)(lds + kKtOff + unit8(i, 4 * stp + hh));
+      const u32x2 hi = *(const __attribute__((address_space(3))) u32x2*)(lds + kKtOff + unit8(i, 4 * stp + 2 + hh));
+      const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+      acc = mfma32x32x16(vt[stp], __builtin_bit_cast(bf16x8, w), acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int d = 64 * vs + 32 * md + 8 * (e >> 2) + 4 * hh + (e & 3);
+      out[d * kLaDim + i] = acc[e];
+    }
+  }
+  if (vs == 0 && tid == 0) glast[(int64_t)bc * H + h] = Glast;
+}
+
+// One workgroup per (request, head, 32 d_v columns); thread: columns d = 32 db + (tid >> 5) + 8 r
+// (r = 0..3), rows i = 4 (tid & 31) .. + 3 of S^T.
+__global__ __launch_bounds__(kLaThreads) void la_scan_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, int H, int maxc,
+    int initial_state, float* __restrict__ pool, int64_t pool_slots, const float* __restrict__ ds,
+    const float* __restrict__ glast, uint16_t* __restrict__ sb) {
+  const int db = blockIdx.x & 3;
+  const int bh = blockIdx.x >> 2;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t slot = slots[b];
+  if (slot < 0 || slot >= pool_slots) return;
+  const int n = cu[b + 1] - cu[b];
+  // chunks beyond the workspace's maxc (a max_seqlen below a request's length) are not read
+  const int nch = min((n + kChunk - 1) / kChunk, maxc);
+  const int tid = threadIdx.x, i4 = tid & 31, dr = tid >> 5;
+  float* sp = pool + (slot * H + h) * (int64_t)(kLaDim * kLaDim);
+  f32x4v S[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int d = 32 * db + dr + 8 * r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[r][e] = initial_state ? sp[(4 * i4 + e) * kLaDim + d] : 0.f;
+  }
+  f32x4v nxt[4];
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const float* src = ds + (((int64_t)b * maxc + c) * H + h) * (kLaDim * kLaDim);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d = 32 * db + dr + 8 * r;
+      nxt[r] = *reinterpret_cast<const f32x4v*>(src + d * kLaDim + 4 * i4);
+    }
+  };
+  if (nch > 0) fetch(0);
+  for (int c = 0; c < nch; ++c) {
+    const int64_t blk = ((int64_t)b * maxc + c) * H + h;
+    uint16_t* dst = sb + blk * (kLaDim * kLaDim);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d = 32 * db + dr + 8 * r;
+      const uint32_t lo = float_to_bf16_bits(S[r][0]) | (float_to_bf16_bits(S[r][1]) << 16);
+      const uint32_t hi = float_to_bf16_bits(S[r][2]) | (float_to_bf16_bits(S[r][3]) << 16);
+      *reinterpret_cast<u32x2*>(dst + d * kLaDim + 4 * i4) = u32x2{lo, hi};
+    }
+    const float decay = __expf(glast[blk]);
+    f32x4v cur[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cur[r] = nxt[r];
+    if (c + 1 < nch) fetch(c + 1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[r] = S[r] * decay + cur[r];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int d = 32 * db + dr + 8 * r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sp[(4 * i4 + e) * kLaDim + d] = S[r][e];
+  }
+}
+
+__global__ __launch_bounds__(kLaThreads) void la_chunk_out_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const int32_t* __restrict__ cu, const int32_t* __restrict__ slots,
+    int H, int maxc, float scale, int initial_state, int64_t pool_slots,
+    const uint16_t* __restrict__ sb, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kLaLds];
+  lds_char_t* lds = (lds_char_t*)lds_raw;
+  const int vs = blockIdx.x & 1;
+  const int rest = blockIdx.x >> 1;
+  const int h = rest % H;
+  const int bc = rest / H;
+  const int b = bc / maxc, c = bc - b * maxc;
+  const int64_t slot = slots[b];
+  if (slot < 0 || slot >= pool_slots) return;
+  const int t_begin = cu[b], n = cu[b + 1] - t_begin;
+  const int c0 = c * kChunk;
+  if (c0 >= n) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int md = wave & 1, nt = wave >> 1;
+  ChunkIn in;
+  load_chunk(in, q, k, v, g, t_begin, n, c0, h, H, vs, true);
+  const float G = wave_inclusive_sum(in.rg);
+  stage_chunk(in, lds, G, 0.f, false, true);
+  if (wave == 0) *(__attribute__((address_space(3))) float*)(lds + kGsOff + 4 * lane) = G;
+  // S_before^T fragments straight from the workspace (A operands: row d, i = 16 stp + 8 hh ..)
+  const bool has_state = c > 0 || initial_state;
+  bf16x8 sa[8];
+  if (has_state) {
+    const uint16_t* src = sb + ((int64_t)bc * H + h) * (kLaDim * kLaDim) +
+                          (int64_t)(64 * vs + 32 * md + l32) * kLaDim + 8 * hh;
+#pragma unroll
+    for (int stp = 0; stp < 8; ++stp) sa[stp] = *reinterpret_cast<const bf16x8*>(src + 16 * stp);
+  }
+  __syncthreads();
+  const int t = 32 * nt + l32;
+  const float Gt = __shfl(G, t, 64);
+  f32x16 o = {};
+  if (has_state) {
+#pragma unroll
+    for (int stp = 0; stp < 8; ++stp)
+      o = mfma32x32x16(sa[stp], lds_read16(lds + kQsOff + chunk16(t, 2 * stp + hh)), o);
+    const float et = __expf(Gt);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] *= et;
+  }
+  bf16x8 vt[4];
+  read_vt_frags(lds, md, vt);
+#pragma unroll
+  for (int ms = 0; ms < 2; ++ms) {
+    if (ms > nt) break;
+    f32x16 a = {};
+#pragma unroll
+    for (int stp = 0; stp < 8; ++stp) {
+      const bf16x8 ka = lds_read16(lds + kKsOff + chunk16(32 * ms + l32, 2 * stp + hh));
+      const bf16x8 qb = lds_read16(lds + kQsOff + chunk16(t, 2 * stp + hh));
+      a = mfma32x32x16(ka, qb, a);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int s = 32 * ms + 8 * (e >> 2) + 4 * hh + (e & 3);
+      const float Gs = *(const __attribute__((address_space(3))) float*)(lds + kGsOff + 4 * s);
+      a[e] = s <= t ? a[e] * __builtin_amdgcn_exp2f((Gt - Gs) * kLog2e) : 0.f;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int e0 = 8 * half;
+      const bf16x8 pb = to_bf16x8(a[e0], a[e0 + 1], a[e0 + 2], a[e0 + 3], a[e0 + 4], a[e0 + 5],
+                                  a[e0 + 6], a[e0 + 7]);
+      o = mfma32x32x16(vt[2 * ms + half], pb, o);
+    }
+  }
+  if (c0 + t < n) {
+    const int64_t hstride = (int64_t)H * kLaDim;
+    uint16_t* orow = out + (int64_t)(t_begin + c0 + t) * hstride + (int64_t)h * kLaDim + 64 * vs + 32 * md + 4 * hh;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const uint32_t lo = float_to_bf16_bits(o[4 * qd] * scale) | (float_to_bf16_bits(o[4 * qd + 1] * scale) << 16);
+      const uint32_t hi = float_to_bf16_bits(o[4 * qd + 2] * scale) | (float_to_bf16_bits(o[4 * qd + 3] * scale) << 16);
+      *reinterpret_cast<u32x2*>(orow + 8 * qd) = u32x2{lo, hi};
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_linear_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -334,6 +612,44 @@ hipError_t launch_linear_prefill(const void* q, const void* k, const void* v, co
   hipLaunchKernelGGL(la_prefill_kernel, dim3((unsigned)grid), dim3(kLaThreads), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, cu, slots, heads,
                      scale, initial_state, pool, pool_slots, (uint16_t*)out);
+  return hipGetLastError();
+}
+
+// Workspace of the chunk-parallel prefill: dS^T (fp32), S_before^T (bf16), G_last, each part
+// 256-byte aligned. Returns the byte size; fills the part offsets if `off` is not null.
+size_t linear_prefill_ws(int64_t batch, int64_t maxc, int64_t heads, size_t* off) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t blocks = (size_t)(batch * maxc * heads);
+  const size_t ds = 0, sb = al(ds + blocks * kLaDim * kLaDim * 4), gl = al(sb + blocks * kLaDim * kLaDim * 2);
+  if (off) { off[0] = ds; off[1] = sb; off[2] = gl; }
+  return al(gl + blocks * 4);
+}
+
+hipError_t launch_linear_prefill_parallel(const void* q, const void* k, const void* v, const float* g,
+                                          const int32_t* cu, const int32_t* slots, int batch, int heads,
+                                          int maxc, float scale, int initial_state, float* pool,
+                                          int64_t pool_slots, void* out, void* ws, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  size_t off[3];
+  linear_prefill_ws(batch, maxc, heads, off);
+  char* w = (char*)ws;
+  float* ds = (float*)(w + off[0]);
+  uint16_t* sb = (uint16_t*)(w + off[1]);
+  float* gl = (float*)(w + off[2]);
+  const int64_t chunk_grid = (int64_t)batch * maxc * heads * 2;
+  if (chunk_grid > 0) {
+    hipLaunchKernelGGL(la_chunk_state_kernel, dim3((unsigned)chunk_grid), dim3(kLaThreads), 0, stream,
+                       (const uint16_t*)k, (const uint16_t*)v, g, cu, heads, maxc, ds, gl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(la_scan_kernel, dim3((unsigned)((int64_t)batch * heads * 4)), dim3(kLaThreads), 0,
+                     stream, cu, slots, heads, maxc, initial_state, pool, pool_slots, ds, gl, sb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || chunk_grid == 0) return e;
+  hipLaunchKernelGGL(la_chunk_out_kernel, dim3((unsigned)chunk_grid), dim3(kLaThreads), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, cu, slots, heads, maxc,
+                     scale, initial_state, pool_slots, sb, (uint16_t*)out);
   return hipGetLastError();
 }
 

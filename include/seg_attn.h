@@ -204,16 +204,24 @@ seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
  * Prefill: request b's tokens are rows cu_seqlens[b] .. cu_seqlens[b+1]-1; its state starts
  * from its slot (initial_state = 1) or from zero (0) and the final state is written back to the
  * slot. Chunks of 64 tokens; the products run on bf16 operands with fp32 accumulation and an
- * fp32 state. Decode: one token per request (row b), state read from and written to the slot,
+ * fp32 state. With a workspace (of seg_attn_linear_prefill_workspace_bytes(batch, max_seqlen,
+ * H, 128) bytes, 256-byte aligned, contents clobbered) all chunks of all requests run in
+ * parallel, with a scan carrying the state between them; max_seqlen (HOST) must be at least every
+ * request's length (longer requests are not processed past it). With workspace = NULL one
+ * workgroup per (request, head, half of d_v) walks the chunks in order and max_seqlen is unused. Decode: one token per request (row b), state read from and written to the slot,
  * in fp32 throughout. Buffers: q, k, v and the pool 16-byte aligned, out 8-byte.
  * Returns SEG_ATTN_OK, or an error before anything is launched.
  */
 seg_attn_status_t seg_attn_linear_prefill(const void* q, const void* k, const void* v,
                                           const float* g, const int32_t* cu_seqlens,
                                           const int32_t* state_slots, int32_t batch,
-                                          int32_t num_heads, int32_t head_dim, float scale,
-                                          int32_t initial_state, float* state_pool,
-                                          int64_t pool_slots, void* out, seg_attn_stream_t stream);
+                                          int32_t max_seqlen, int32_t num_heads, int32_t head_dim,
+                                          float scale, int32_t initial_state, float* state_pool,
+                                          int64_t pool_slots, void* out, void* workspace,
+                                          size_t workspace_bytes, seg_attn_stream_t stream);
+/* Workspace bytes of the chunk-parallel linear prefill (0 for invalid or unsupported sizes). */
+size_t seg_attn_linear_prefill_workspace_bytes(int32_t batch, int32_t max_seqlen, int32_t num_heads,
+                                               int32_t head_dim);
 seg_attn_status_t seg_attn_linear_decode(const void* q, const void* k, const void* v, const float* g,
                                          const int32_t* state_slots, int32_t batch,
                                          int32_t num_heads, int32_t head_dim, float scale,

@@ -120,17 +120,18 @@ def test_kv_append_without_new_tokens_is_a_noop():
 
 
 def _linear_args(**over):
-    a = dict(q=256, k=256, v=256, g=256, cu=1, slots=1, batch=2, h=16, d=128, scale=0.1, init=1,
-             pool=256, npool=4, out=256, stream=None)
+    a = dict(q=256, k=256, v=256, g=256, cu=1, slots=1, batch=2, maxl=100, h=16, d=128, scale=0.1,
+             init=1, pool=256, npool=4, out=256, ws=None, wsb=0, stream=None)
     a.update(over)
-    return [a[k] for k in ("q", "k", "v", "g", "cu", "slots", "batch", "h", "d", "scale", "init",
-                           "pool", "npool", "out", "stream")]
+    return [a[k] for k in ("q", "k", "v", "g", "cu", "slots", "batch", "maxl", "h", "d", "scale",
+                           "init", "pool", "npool", "out", "ws", "wsb", "stream")]
 
 
 @pytest.mark.parametrize("over,status", [
     (dict(q=None), 1), (dict(pool=None), 1), (dict(cu=None), 1), (dict(batch=-1), 1), (dict(h=0), 1),
     (dict(d=64), 2), (dict(init=2), 1), (dict(scale=float("inf")), 1), (dict(npool=-1), 1),
-    (dict(k=264), 1), (dict(out=260), 1), (dict(batch=0), 0),
+    (dict(k=264), 1), (dict(out=260), 1), (dict(batch=0), 0), (dict(maxl=-1), 1),
+    (dict(ws=512, wsb=1024), 3), (dict(ws=520, wsb=1 << 40), 1),
 ])
 def test_linear_prefill_rejects_bad_arguments(over, status):
     lib = _lib()
@@ -144,9 +145,20 @@ def test_linear_prefill_rejects_bad_arguments(over, status):
 def test_linear_decode_rejects_bad_arguments(over, status):
     lib = _lib()
     a = _linear_args(**over)
-    del a[10]  # no initial_state
-    del a[4]   # no cu_seqlens
+    del a[15:17]  # no workspace
+    del a[11]     # no initial_state
+    del a[7]      # no max_seqlen
+    del a[4]      # no cu_seqlens
     assert lib.seg_attn_linear_decode(*a) == status
+
+
+def test_linear_prefill_workspace_size():
+    _lib()
+    lib = sa._load()
+    # dS^T fp32 + S_before^T bf16 per (request, chunk, head), plus one float each
+    n = lib.seg_attn_linear_prefill_workspace_bytes(2, 1024, 16, 128)
+    assert n >= 2 * 16 * 16 * (128 * 128 * 6 + 4)
+    assert lib.seg_attn_linear_prefill_workspace_bytes(2, 1024, 16, 64) == 0
 
 
 def test_split_plan_and_workspace_size():

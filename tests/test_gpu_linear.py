@@ -44,18 +44,18 @@ def _oracle(w, pool_before):
                                    w.cu_seqlens.cpu().numpy(), s0, w.scale)
 
 
-def _run(w):
+def _run(w, parallel=True):
     sa = _sa()
     if w.kind == "decode":
         return sa.linear_decode(w.q, w.k, w.v, w.g, w.state_slots, w.state_pool, scale=w.scale)
     return sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool,
-                             initial_state=w.initial_state, scale=w.scale)
+                             initial_state=w.initial_state, scale=w.scale, parallel=parallel)
 
 
-def _check(w, name):
+def _check(w, name, parallel=True):
     pool_before = w.state_pool.detach().cpu().clone()
     o_ref, st_ref = _oracle(w, pool_before)
-    out = _run(w)
+    out = _run(w, parallel)
     torch.cuda.synchronize()
     _assert_rel(out.float().cpu().numpy(), o_ref, name)
     pool_after = w.state_pool.detach().cpu()
@@ -71,13 +71,14 @@ def _check(w, name):
 
 
 @needs_gpu
+@pytest.mark.parametrize("parallel", [True, False], ids=["chunk-parallel", "sequential"])
 @pytest.mark.parametrize("initial_state", [False, True])
-def test_linear_prefill_ragged(initial_state):
+def test_linear_prefill_ragged(initial_state, parallel):
     """Lengths around the 64-token chunk: 1, 63, 64, 65, 130, an empty request."""
-    print(f"[case] linear prefill ragged initial_state={initial_state}", flush=True)
+    print(f"[case] linear prefill ragged initial_state={initial_state} parallel={parallel}", flush=True)
     w = wl.make_linear(31, [1, 63, 64, 65, 130, 0], kind="prefill", initial_state=initial_state,
                        num_heads=4).to("cuda")
-    _check(w, f"la-ragged-{int(initial_state)}")
+    _check(w, f"la-ragged-{int(initial_state)}-{int(parallel)}", parallel)
 
 
 @needs_gpu
@@ -87,6 +88,21 @@ def test_linear_named_workloads(name):
     print(f"[case] linear {name}", flush=True)
     w = wl.make_linear_config(name, device="cuda")
     _check(w, name)
+
+
+@needs_gpu
+def test_linear_sequential_prefill_full_size():
+    print("[case] linear la_prefill_b2_1024 sequential", flush=True)
+    w = wl.make_linear_config("la_prefill_b2_1024", device="cuda")
+    _check(w, "la_prefill_b2_1024-sequential", parallel=False)
+
+
+@needs_gpu
+def test_linear_parallel_prefill_long_request_with_state():
+    """A 3000-token request (47 chunks) next to short ones, from stored states."""
+    print("[case] linear prefill long request", flush=True)
+    w = wl.make_linear(36, [3000, 5, 200], kind="prefill", initial_state=True, num_heads=2).to("cuda")
+    _check(w, "la-long")
 
 
 @needs_gpu
@@ -137,15 +153,16 @@ def test_linear_decode_equals_one_token_prefill():
 
 
 @needs_gpu
-def test_linear_prefill_is_deterministic():
+@pytest.mark.parametrize("parallel", [True, False], ids=["chunk-parallel", "sequential"])
+def test_linear_prefill_is_deterministic(parallel):
     sa = _sa()
-    print("[case] linear prefill determinism", flush=True)
+    print(f"[case] linear prefill determinism parallel={parallel}", flush=True)
     w = wl.make_linear(35, [300, 77], kind="prefill", num_heads=4).to("cuda")
     pool0 = w.state_pool.clone()
-    o1 = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool)
+    o1 = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool, parallel=parallel)
     p1 = w.state_pool.clone()
     w.state_pool.copy_(pool0)
-    o2 = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool)
+    o2 = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool, parallel=parallel)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(p1.view(torch.int32), w.state_pool.view(torch.int32))
