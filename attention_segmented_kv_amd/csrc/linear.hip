@@ -459,63 +459,62 @@ __global__ __launch_bounds__(kLaThreads) void la_chunk_state_kernel(
   if (vs == 0 && tid == 0) glast[(int64_t)bc * H + h] = Glast;
 }
 
-// One workgroup per (request, head, 32 d_v columns); thread: columns d = 32 db + (tid >> 5) + 8 r
-// (r = 0..3), rows i = 4 (tid & 31) .. + 3 of S^T.
+// One workgroup per (request, head, 8 d_v columns); thread: column d = 8 db + (tid >> 5), rows
+// i = 4 (tid & 31) .. + 3 of S^T. The chain S <- exp(G_last) S + dS is one fma per chunk, so the
+// loop is bounded by the loads: the next kScanDepth chunks' dS and G_last are always in flight.
+constexpr int kScanCols = 8;
+constexpr int kScanDepth = 8;
+
 __global__ __launch_bounds__(kLaThreads) void la_scan_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, int H, int maxc,
     int initial_state, float* __restrict__ pool, int64_t pool_slots, const float* __restrict__ ds,
     const float* __restrict__ glast, uint16_t* __restrict__ sb) {
-  const int db = blockIdx.x & 3;
-  const int bh = blockIdx.x >> 2;
+  constexpr int kGroups = kLaDim / kScanCols;
+  const int db = blockIdx.x % kGroups;
+  const int bh = blockIdx.x / kGroups;
   const int b = bh / H, h = bh - b * H;
   const int64_t slot = slots[b];
   if (slot < 0 || slot >= pool_slots) return;
   const int n = cu[b + 1] - cu[b];
   // chunks beyond the workspace's maxc (a max_seqlen below a request's length) are not read
   const int nch = min((n + kChunk - 1) / kChunk, maxc);
-  const int tid = threadIdx.x, i4 = tid & 31, dr = tid >> 5;
+  const int tid = threadIdx.x, i4 = tid & 31;
+  const int d = kScanCols * db + (tid >> 5);
   float* sp = pool + (slot * H + h) * (int64_t)(kLaDim * kLaDim);
-  f32x4v S[4];
+  f32x4v S;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int d = 32 * db + dr + 8 * r;
+  for (int e = 0; e < 4; ++e) S[e] = initial_state ? sp[(4 * i4 + e) * kLaDim + d] : 0.f;
+  const int64_t blk0 = (int64_t)b * maxc * H + h;  // block of chunk c: blk0 + c * H
+  const float* dsrc = ds + blk0 * (kLaDim * kLaDim) + d * kLaDim + 4 * i4;
+  const int64_t cstride = (int64_t)H * kLaDim * kLaDim;
+  f32x4v ring[kScanDepth];
+  float gring[kScanDepth];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) S[r][e] = initial_state ? sp[(4 * i4 + e) * kLaDim + d] : 0.f;
-  }
-  f32x4v nxt[4];
-  auto fetch = [&](int c) __attribute__((always_inline)) {
-    const float* src = ds + (((int64_t)b * maxc + c) * H + h) * (kLaDim * kLaDim);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d = 32 * db + dr + 8 * r;
-      nxt[r] = *reinterpret_cast<const f32x4v*>(src + d * kLaDim + 4 * i4);
+  for (int j = 0; j < kScanDepth; ++j) {
+    if (j < nch) {
+      ring[j] = *reinterpret_cast<const f32x4v*>(dsrc + j * cstride);
+      gring[j] = glast[blk0 + (int64_t)j * H];
     }
-  };
-  if (nch > 0) fetch(0);
-  for (int c = 0; c < nch; ++c) {
-    const int64_t blk = ((int64_t)b * maxc + c) * H + h;
-    uint16_t* dst = sb + blk * (kLaDim * kLaDim);
+  }
+  uint16_t* dst = sb + blk0 * (kLaDim * kLaDim) + d * kLaDim + 4 * i4;
+  for (int cb = 0; cb < nch; cb += kScanDepth) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d = 32 * db + dr + 8 * r;
-      const uint32_t lo = float_to_bf16_bits(S[r][0]) | (float_to_bf16_bits(S[r][1]) << 16);
-      const uint32_t hi = float_to_bf16_bits(S[r][2]) | (float_to_bf16_bits(S[r][3]) << 16);
-      *reinterpret_cast<u32x2*>(dst + d * kLaDim + 4 * i4) = u32x2{lo, hi};
+    for (int j = 0; j < kScanDepth; ++j) {
+      const int c = cb + j;
+      if (c < nch) {
+        const uint32_t lo = float_to_bf16_bits(S[0]) | (float_to_bf16_bits(S[1]) << 16);
+        const uint32_t hi = float_to_bf16_bits(S[2]) | (float_to_bf16_bits(S[3]) << 16);
+        *reinterpret_cast<u32x2*>(dst + c * cstride) = u32x2{lo, hi};
+        S = S * __expf(gring[j]) + ring[j];
+        if (c + kScanDepth < nch) {
+          ring[j] = *reinterpret_cast<const f32x4v*>(dsrc + (c + kScanDepth) * cstride);
+          gring[j] = glast[blk0 + (int64_t)(c + kScanDepth) * H];
+        }
+      }
     }
-    const float decay = __expf(glast[blk]);
-    f32x4v cur[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cur[r] = nxt[r];
-    if (c + 1 < nch) fetch(c + 1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S[r] = S[r] * decay + cur[r];
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int d = 32 * db + dr + 8 * r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sp[(4 * i4 + e) * kLaDim + d] = S[r][e];
-  }
+  for (int e = 0; e < 4; ++e) sp[(4 * i4 + e) * kLaDim + d] = S[e];
 }
 
 __global__ __launch_bounds__(kLaThreads) void la_chunk_out_kernel(
@@ -643,7 +642,8 @@ hipError_t launch_linear_prefill_parallel(const void* q, const void* k, const vo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(la_scan_kernel, dim3((unsigned)((int64_t)batch * heads * 4)), dim3(kLaThreads), 0,
+  hipLaunchKernelGGL(la_scan_kernel, dim3((unsigned)((int64_t)batch * heads * (kLaDim / kScanCols))),
+                     dim3(kLaThreads), 0,
                      stream, cu, slots, heads, maxc, initial_state, pool, pool_slots, ds, gl, sb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || chunk_grid == 0) return e;
