@@ -38,17 +38,17 @@ __device__ __forceinline__ uint32_t pack_fp8x2(float a, float b) {
 }
 
 // x / s correctly rounded, from r = 1/s correctly rounded: q = x r, then two corrections
-// q += (x - q s) r, each residual exact in an fma. After the first correction q is within one
+// q -= (q s - x) r, each residual exact in an fma. After the first correction q is within one
 // ulp of x / s, and then the residual step rounds correctly (Markstein's theorem on division by
 // a correctly rounded reciprocal; it needs no underflow in the residuals, which the callers'
 // range of s, 2^-80 .. 2^80, ensures for every quotient of magnitude 2^-11 or more, and smaller
-// quotients encode as a signed zero either way). The sign is taken from x so that x = -0
-// keeps its sign.
+// quotients encode as a signed zero either way). Written with the negated residual so that
+// x = -0 keeps its sign: (q s - x) is then +0 and -0 - (+0) r stays -0.
 __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
   float q = __fmul_rn(x, r);
-  q = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
-  q = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
-  return __builtin_copysignf(q, x);
+  q = __builtin_fmaf(-__builtin_fmaf(q, s, -x), r, q);
+  q = __builtin_fmaf(-__builtin_fmaf(q, s, -x), r, q);
+  return q;
 }
 
 // Lane data movement inside the 16-lane DPP rows, which are the row groups: kCtrl is a DPP
@@ -121,26 +121,12 @@ __device__ __forceinline__ uint32_t group_ballot(bool p) {
   return (uint32_t)(__ballot(p) >> shift) & 0xFFFFu;
 }
 
-// kFmt: 0 = bf16 pool (copy), 1 = FP8 (E4M3FN) pool, 2 = INT8 pool.
-template <int kFmt>
-__global__ __launch_bounds__(256) void kv_append_kernel(
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const Seg* __restrict__ segs, const int32_t* __restrict__ seg_indptr,
-    const int32_t* __restrict__ cu_new, const int32_t* __restrict__ cu_k, int batch, int total_new,
-    int hkv, int64_t pool_tokens, void* __restrict__ k_pool, void* __restrict__ v_pool,
-    float* __restrict__ k_scale, float* __restrict__ v_scale) {
-  // rows number fewer than 2^31 (checked by the caller), so 32-bit index arithmetic suffices
-  const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
-  if (row >= (uint32_t)total_new * (uint32_t)hkv) return;  // whole 16-lane groups leave together
-  const int sub = threadIdx.x & 15;                         // values 8 sub .. 8 sub + 7 of the row
-  const int t = (int)(row / (uint32_t)hkv);
-  const int h = (int)(row - (uint32_t)t * (uint32_t)hkv);
-
-  // the row's values are loaded first: they do not depend on where the row goes
-  const int64_t src = (int64_t)row * 128 + 8 * sub;
-  const u32x4 kraw = *reinterpret_cast<const u32x4*>(k_new + src);
-  const u32x4 vraw = *reinterpret_cast<const u32x4*>(v_new + src);
-
+// Pool slot of new token t (all 16 lanes of the calling group take part and get the result), or
+// -1 when the tables do not give it one.
+__device__ __forceinline__ int64_t find_slot(int t, int sub, const Seg* __restrict__ segs,
+                                             const int32_t* __restrict__ seg_indptr,
+                                             const int32_t* __restrict__ cu_new,
+                                             const int32_t* __restrict__ cu_k, int batch) {
   // Request of token t: the largest b with cu_new[b] <= t (requests without new tokens have
   // cu_new[b] == cu_new[b + 1] and are passed over). The group's 16 lanes probe 16 evenly
   // spaced entries of [lo, hi) at once, which shrinks the range 16-fold per step: one step for
@@ -176,15 +162,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     }
     before += __shfl(incl, 15, 16);
   }
-  // a key outside the request's segments or the pool means inconsistent tables: nothing is
-  // written for it rather than a write out of bounds
-  if (j < 0 || slot < 0 || slot >= pool_tokens) return;
+  return j < 0 ? -1 : slot;
+}
 
-  const int64_t dst_row = slot * hkv + h;
-  if constexpr (kFmt == 0) {
-    __builtin_nontemporal_store(kraw, reinterpret_cast<u32x4*>((uint16_t*)k_pool + dst_row * 128 + 8 * sub));
-    __builtin_nontemporal_store(vraw, reinterpret_cast<u32x4*>((uint16_t*)v_pool + dst_row * 128 + 8 * sub));
-  } else {
+// Quantise one (token, kv head) row of K and of V (8 values per lane of the 16-lane group) and
+// store codes and scales at pool row dst_row.
+template <int kFmt>
+__device__ __forceinline__ void quantise_row_pair(const u32x4 kraw, const u32x4 vraw, int sub,
+                                                  int64_t dst_row, uint8_t* __restrict__ k_pool,
+                                                  uint8_t* __restrict__ v_pool,
+                                                  float* __restrict__ k_scale,
+                                                  float* __restrict__ v_scale) {
     // K and V rows side by side: row maxima over the group, scales, quotients, codes
     float xk[8], xv[8];
     unpack_bf16x8(kraw, xk);
@@ -219,11 +207,86 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const int64_t dst = dst_row * 128 + 8 * sub;
     const u32x2 ck = kFmt == 1 ? encode_fp8x8(yk) : encode_int8x8(yk);
     const u32x2 cv = kFmt == 1 ? encode_fp8x8(yv) : encode_int8x8(yv);
-    __builtin_nontemporal_store(ck, reinterpret_cast<u32x2*>((uint8_t*)k_pool + dst));
-    __builtin_nontemporal_store(cv, reinterpret_cast<u32x2*>((uint8_t*)v_pool + dst));
+    __builtin_nontemporal_store(ck, reinterpret_cast<u32x2*>(k_pool + dst));
+    __builtin_nontemporal_store(cv, reinterpret_cast<u32x2*>(v_pool + dst));
     if (sub == 0) {
       k_scale[dst_row] = sk;
       v_scale[dst_row] = sv;
+    }
+}
+
+// kFmt: 0 = bf16 pool (copy), 1 = FP8 (E4M3FN) pool, 2 = INT8 pool.
+template <int kFmt>
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const Seg* __restrict__ segs, const int32_t* __restrict__ seg_indptr,
+    const int32_t* __restrict__ cu_new, const int32_t* __restrict__ cu_k, int batch, int total_new,
+    int hkv, int64_t pool_tokens, void* __restrict__ k_pool, void* __restrict__ v_pool,
+    float* __restrict__ k_scale, float* __restrict__ v_scale) {
+  // rows number fewer than 2^31 (checked by the caller), so 32-bit index arithmetic suffices
+  const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  if (row >= (uint32_t)total_new * (uint32_t)hkv) return;  // whole 16-lane groups leave together
+  const int sub = threadIdx.x & 15;                         // values 8 sub .. 8 sub + 7 of the row
+  const int t = (int)(row / (uint32_t)hkv);
+  const int h = (int)(row - (uint32_t)t * (uint32_t)hkv);
+
+  // the row's values are loaded first: they do not depend on where the row goes
+  const int64_t src = (int64_t)row * 128 + 8 * sub;
+  const u32x4 kraw = *reinterpret_cast<const u32x4*>(k_new + src);
+  const u32x4 vraw = *reinterpret_cast<const u32x4*>(v_new + src);
+
+  const int64_t slot = find_slot(t, sub, segs, seg_indptr, cu_new, cu_k, batch);
+  // a key outside the request's segments or the pool means inconsistent tables: nothing is
+  // written for it rather than a write out of bounds
+  if (slot < 0 || slot >= pool_tokens) return;
+
+  const int64_t dst_row = slot * hkv + h;
+  if constexpr (kFmt == 0) {
+    __builtin_nontemporal_store(kraw, reinterpret_cast<u32x4*>((uint16_t*)k_pool + dst_row * 128 + 8 * sub));
+    __builtin_nontemporal_store(vraw, reinterpret_cast<u32x4*>((uint16_t*)v_pool + dst_row * 128 + 8 * sub));
+  } else {
+    quantise_row_pair<kFmt>(kraw, vraw, sub, dst_row, (uint8_t*)k_pool, (uint8_t*)v_pool, k_scale, v_scale);
+  }
+}
+
+// FP8 / INT8 pools: one 16-lane group per new token, all of its kv heads. The slot lookup is
+// done once per token, and the rows of up to 8 heads are loaded before any is quantised.
+constexpr int kHeadsPerPass = 8;
+constexpr int kTokenPathMin = 4096;  // new tokens from which the per-token kernel is used
+
+template <int kFmt>
+__global__ __launch_bounds__(256) void kv_append_token_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const Seg* __restrict__ segs, const int32_t* __restrict__ seg_indptr,
+    const int32_t* __restrict__ cu_new, const int32_t* __restrict__ cu_k, int batch, int total_new,
+    int hkv, int64_t pool_tokens, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    float* __restrict__ k_scale, float* __restrict__ v_scale) {
+  const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  if (t >= total_new) return;  // whole 16-lane groups leave together
+  const int sub = threadIdx.x & 15;
+  const int64_t src0 = (int64_t)t * hkv * 128 + 8 * sub;
+  u32x4 kraw[kHeadsPerPass], vraw[kHeadsPerPass];
+  auto load_pass = [&](int h0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kHeadsPerPass; ++i) {
+      if (h0 + i < hkv) {
+        kraw[i] = *reinterpret_cast<const u32x4*>(k_new + src0 + (int64_t)(h0 + i) * 128);
+        vraw[i] = *reinterpret_cast<const u32x4*>(v_new + src0 + (int64_t)(h0 + i) * 128);
+      }
+    }
+  };
+  load_pass(0);  // in flight during the lookup
+  const int64_t slot = find_slot(t, sub, segs, seg_indptr, cu_new, cu_k, batch);
+  // a key outside the request's segments or the pool means inconsistent tables: nothing is
+  // written for it rather than a write out of bounds
+  if (slot < 0 || slot >= pool_tokens) return;
+  for (int h0 = 0; h0 < hkv; h0 += kHeadsPerPass) {
+    if (h0 > 0) load_pass(h0);
+#pragma unroll
+    for (int i = 0; i < kHeadsPerPass; ++i) {
+      if (h0 + i < hkv)
+        quantise_row_pair<kFmt>(kraw[i], vraw[i], sub, slot * hkv + h0 + i, k_pool, v_pool, k_scale,
+                                v_scale);
     }
   }
 }
@@ -239,10 +302,20 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const void* se
   if (rows == 0) return hipSuccess;
   if (rows > INT32_MAX) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
-  auto kern = fmt == 2 ? kv_append_kernel<2> : (fmt == 1 ? kv_append_kernel<1> : kv_append_kernel<0>);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, (const uint16_t*)k_new,
-                     (const uint16_t*)v_new, (const Seg*)segs, seg_indptr, cu_new, cu_k, batch,
-                     total_new, hkv, pool_tokens, k_pool, v_pool, k_scale, v_scale);
+  // FP8 / INT8: one group per token (one lookup per token) once there are enough tokens to fill
+  // the chip with it; below that, one group per (token, head) row keeps more groups in flight.
+  if (fmt == 0 || total_new < kTokenPathMin) {
+    auto kern = fmt == 2 ? kv_append_kernel<2> : (fmt == 1 ? kv_append_kernel<1> : kv_append_kernel<0>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, (const Seg*)segs, seg_indptr, cu_new, cu_k, batch,
+                       total_new, hkv, pool_tokens, k_pool, v_pool, k_scale, v_scale);
+  } else {
+    const unsigned tgrid = (unsigned)((total_new + kRowsPerBlock - 1) / kRowsPerBlock);
+    auto kern = fmt == 2 ? kv_append_token_kernel<2> : kv_append_token_kernel<1>;
+    hipLaunchKernelGGL(kern, dim3(tgrid), dim3(256), 0, stream, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, (const Seg*)segs, seg_indptr, cu_new, cu_k, batch,
+                       total_new, hkv, pool_tokens, (uint8_t*)k_pool, (uint8_t*)v_pool, k_scale, v_scale);
+  }
   return hipGetLastError();
 }
 
