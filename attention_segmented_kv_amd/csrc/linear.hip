@@ -94,13 +94,17 @@ __global__ __launch_bounds__(kLaThreads) void la_decode_kernel(
 //   Vt     [64 d][64 s]:  V^T of the half, 8-byte unit u of row r at u ^ (r % 16)
 //   Kt     [128 i][64 s]: K~^T, same 8-byte swizzle
 //   Gs     [64] fp32:      the chunk's running decay sums
+// Ordered so that the chunk-output kernel, which needs only Qs, Ks, Vt and Gs, takes the first
+// 40.25 KiB, and the chunk-state kernel, which needs Vt and Kt, the first 56.25 KiB.
 constexpr int kQsOff = 0;                              // Qs: 16 KiB
 constexpr int kKsOff = kQsOff + kChunk * kLaDim * 2;   // Ks: 16 KiB
-constexpr int kStOff = kKsOff + kChunk * kLaDim * 2;   // St: 16 KiB
-constexpr int kVtOff = kStOff + 64 * kLaDim * 2;       // Vt: 8 KiB
-constexpr int kKtOff = kVtOff + 64 * kChunk * 2;       // Kt: 16 KiB
-constexpr int kGsOff = kKtOff + kLaDim * kChunk * 2;   // Gs: 256 B
-constexpr int kLaLds = kGsOff + kChunk * 4;            // 72.25 KiB in all
+constexpr int kVtOff = kKsOff + kChunk * kLaDim * 2;   // Vt: 8 KiB
+constexpr int kGsOff = kVtOff + 64 * kChunk * 2;       // Gs: 256 B
+constexpr int kOutLds = kGsOff + kChunk * 4;           // 40.25 KiB
+constexpr int kKtOff = kOutLds;                        // Kt: 16 KiB
+constexpr int kStateLds = kKtOff + kLaDim * kChunk * 2;  // 56.25 KiB
+constexpr int kStOff = kStateLds;                      // St: 16 KiB
+constexpr int kLaLds = kStOff + 64 * kLaDim * 2;       // 72.25 KiB in all
 
 __device__ __forceinline__ int chunk16(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 __device__ __forceinline__ int unit8(int r, int u) { return r * 128 + ((u ^ (r & 15)) << 3); }
@@ -418,7 +422,7 @@ __device__ __forceinline__ void read_vt_frags(const lds_char_t* lds, int md, bf1
 __global__ __launch_bounds__(kLaThreads) void la_chunk_state_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ g,
     const int32_t* __restrict__ cu, int H, int maxc, float* __restrict__ ds, float* __restrict__ glast) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kLaLds];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kStateLds];
   lds_char_t* lds = (lds_char_t*)lds_raw;
   const int vs = blockIdx.x & 1;
   const int rest = blockIdx.x >> 1;
@@ -522,7 +526,7 @@ __global__ __launch_bounds__(kLaThreads) void la_chunk_out_kernel(
     const float* __restrict__ g, const int32_t* __restrict__ cu, const int32_t* __restrict__ slots,
     int H, int maxc, float scale, int initial_state, int64_t pool_slots,
     const uint16_t* __restrict__ sb, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kLaLds];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kOutLds];
   lds_char_t* lds = (lds_char_t*)lds_raw;
   const int vs = blockIdx.x & 1;
   const int rest = blockIdx.x >> 1;
