@@ -541,10 +541,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   // for even r and r * P + P - 1 - p for odd r; in round r its workgroups take kv heads
   // (g + r) % hkv, so the 8 heads of each chunk are all done and every workgroup meets every
   // head: the reading speed of a head's slices of the pool rows varies, and this keeps the
-  // workgroups even.
+  // workgroups even. Workgroups are numbered g * P + p: with P a multiple of 8, the workgroups
+  // of one column, which read the same chunk's rows in every round, are dispatched to the same
+  // XCD and share its L2 (a 128-byte line of the FP8 / INT8 scale arrays holds 4 tokens x 8
+  // heads; spread over 8 XCDs it was fetched 8 times).
   const int P = gridDim.x / hkv;
-  const int p = rfl(blockIdx.x / hkv);
-  const int g = rfl(blockIdx.x - p * hkv);
+  const int g = rfl(blockIdx.x / P);
+  const int p = rfl(blockIdx.x - g * P);
   const int full_rounds = n_chunks / P;
   const int last_pos = (full_rounds & 1) ? P - 1 - p : p;
   const int my_units = full_rounds + (last_pos < n_chunks - full_rounds * P ? 1 : 0);
