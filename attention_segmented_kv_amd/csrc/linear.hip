@@ -127,8 +127,12 @@ __global__ __launch_bounds__(kLaThreads) void la_prefill_kernel(
     uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kLaLds];
   lds_char_t* lds = (lds_char_t*)lds_raw;
-  const int vs = blockIdx.x & 1;
-  const int bh = blockIdx.x >> 1;
+  // the two d_v halves of a (request, head) are workgroups bh and bh + gridDim.x / 2: with
+  // gridDim.x / 2 a multiple of 8 they are dispatched to the same XCD and read q, k through
+  // one L2
+  const int half_grid = gridDim.x >> 1;
+  const int vs = blockIdx.x >= half_grid;
+  const int bh = blockIdx.x - vs * half_grid;
   const int b = bh / H, h = bh - b * H;
   const int64_t slot = slots[b];
   if (slot < 0 || slot >= pool_slots) return;  // the whole workgroup leaves together
@@ -424,8 +428,10 @@ __global__ __launch_bounds__(kLaThreads) void la_chunk_state_kernel(
     const int32_t* __restrict__ cu, int H, int maxc, float* __restrict__ ds, float* __restrict__ glast) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kStateLds];
   lds_char_t* lds = (lds_char_t*)lds_raw;
-  const int vs = blockIdx.x & 1;
-  const int rest = blockIdx.x >> 1;
+  // halves of a (request, chunk, head) as in la_prefill_kernel: same XCD, one L2 for q and k
+  const int half_grid = gridDim.x >> 1;
+  const int vs = blockIdx.x >= half_grid;
+  const int rest = blockIdx.x - vs * half_grid;
   const int h = rest % H;
   const int bc = rest / H;  // b * maxc + c
   const int b = bc / maxc, c = bc - b * maxc;
@@ -528,8 +534,10 @@ __global__ __launch_bounds__(kLaThreads) void la_chunk_out_kernel(
     const uint16_t* __restrict__ sb, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kOutLds];
   lds_char_t* lds = (lds_char_t*)lds_raw;
-  const int vs = blockIdx.x & 1;
-  const int rest = blockIdx.x >> 1;
+  // halves of a (request, chunk, head) as in la_prefill_kernel: same XCD, one L2 for q and k
+  const int half_grid = gridDim.x >> 1;
+  const int vs = blockIdx.x >= half_grid;
+  const int rest = blockIdx.x - vs * half_grid;
   const int h = rest % H;
   const int bc = rest / H;
   const int b = bc / maxc, c = bc - b * maxc;
