@@ -5,7 +5,7 @@
 // FlashAccel article ("data layout": attention computed per block of the KV, then reduced per
 // request). A one-workgroup plan kernel lists the chunks of all requests on the device, so no
 // launch slot is spent on requests shorter than the longest, and chooses `len` from the total
-// key count so that every compute unit gets about a dozen units.
+// key count so that every compute unit gets about 6 units.
 //
 // Split pass. One persistent workgroup per compute unit walks its share of the units. Its 4
 // waves split each unit's tiles round robin (tile i to wave i % 4) and stream them through a
@@ -1023,9 +1023,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
 
 }  // namespace
 
-// Units per workgroup the automatic chunk length aims at: one per kv head, so that with the
-// per-round head rotation every workgroup meets each head about once.
-constexpr int kUnitsPerWorkgroup = 8;
+// Units per workgroup the automatic chunk length aims at. Measured over 4, 6, 8, 12 and 16 on
+// the bf16 batch-128 and the FP8 / INT8 batch-16 long-context decodes: 6 was the fastest or
+// within 1% of it on each; 4 leaves the longest requests' chunks too long to balance, 12 and
+// more pay for the extra partial results and merge work.
+constexpr int kUnitsPerWorkgroup = 6;
 
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int kv, const void* segs,
