@@ -148,6 +148,19 @@ def _check_tables(segs, seg_indptr, cu, device, batch_plus_1, names):
             raise ValueError(f"{nm} must have batch + 1 entries")
 
 
+def _check_workspace(ws: torch.Tensor, device: torch.device):
+    """A caller-supplied workspace: a contiguous byte tensor on the device of the other operands
+    (its size is checked by the library)."""
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+    if ws.dtype != torch.uint8:
+        raise TypeError(f"workspace has dtype {ws.dtype}, expected torch.uint8")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
 def prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Tensor,
             seg_indptr: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
             max_seqlen_q: int, max_seqlen_k: int, *, causal: bool = True,
@@ -216,18 +229,9 @@ def decode_workspace_bytes(batch: int, max_seqlen_k: int, num_heads_q: int = 64,
                                                       head_dim, kv_dtype, num_splits))
 
 
-def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Tensor,
-           seg_indptr: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, *,
-           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
-           softmax_scale: Optional[float] = None, num_splits: int = 0,
-           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           workspace: Optional[torch.Tensor] = None, return_lse: bool = False):
-    """Single-token decode with split-K and a log-sum-exp merge; see seg_attn_decode.
-
-    q [B, Hq, 128] bf16; k_pool/v_pool [pool_tokens, Hkv, 128] bf16, or float8_e4m3fn / int8
-    codes with k_scale/v_scale [pool_tokens, Hkv] fp32. A workspace is allocated here unless
-    given."""
-    lib = _load()
+def _decode_args(q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_k, k_scale, v_scale, softmax_scale,
+                 out, lse, return_lse):
+    """Argument checks of decode; allocates out / lse when not given."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("q must be a GPU tensor")
@@ -263,6 +267,29 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: to
         lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
     if lse is not None:
         _check(lse, "lse", (torch.float32,), dev, 2)
+        if tuple(lse.shape) != (batch, hq):
+            raise ValueError("lse must have shape [B, Hq]")
+    return dev, kv_dtype, batch, hq, hkv, d, pool_tokens, float(softmax_scale), out, lse
+
+
+def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Tensor,
+           seg_indptr: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, *,
+           k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+           softmax_scale: Optional[float] = None, num_splits: int = 0,
+           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Single-token decode with split-K and a log-sum-exp merge; see seg_attn_decode.
+
+    q [B, Hq, 128] bf16; k_pool/v_pool [pool_tokens, Hkv, 128] bf16, or float8_e4m3fn / int8
+    codes with k_scale/v_scale [pool_tokens, Hkv] fp32. A workspace is allocated here unless
+    given."""
+    lib = _load()
+    dev, kv_dtype, batch, hq, hkv, d, pool_tokens, scale, out, lse = _decode_args(
+        q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_k, k_scale, v_scale, softmax_scale, out, lse,
+        return_lse)
+    scaled = kv_dtype != KV_BF16
+    if workspace is not None:
+        _check_workspace(workspace, dev)
     with torch.cuda.device(dev):
         need = int(lib.seg_attn_decode_workspace_bytes(batch, int(max_seqlen_k), hq, hkv, d, kv_dtype,
                                                        int(num_splits)))
@@ -270,11 +297,11 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: to
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.seg_attn_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
-                                 kv_dtype, _ptr(segs), _ptr(seg_indptr), _ptr(cu_seqlens_k), batch,
-                                 int(max_seqlen_k), hq, hkv, d, pool_tokens, float(softmax_scale),
-                                 int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-                                 stream)
+        st = lib.seg_attn_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale if scaled else None),
+                                 _ptr(v_scale if scaled else None), kv_dtype, _ptr(segs),
+                                 _ptr(seg_indptr), _ptr(cu_seqlens_k), batch, int(max_seqlen_k), hq,
+                                 hkv, d, pool_tokens, scale, int(num_splits), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), ws_bytes, stream)
     if st != 0:
         raise SegAttnError("seg_attn_decode", st)
     return (out, lse) if return_lse else out
@@ -382,6 +409,8 @@ def linear_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
         need = int(lib.seg_attn_linear_prefill_workspace_bytes(batch, int(max_seqlen), H, D))
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        else:
+            _check_workspace(workspace, dev)
         ws_bytes = workspace.numel() * workspace.element_size()
     else:
         workspace = None

@@ -18,9 +18,9 @@ hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int kv, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,
-                         int forced_len, int min_len, int max_chunks, int cu_count, float scale,
-                         void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* recs,
-                         float* ws_o, float* ws_lse, hipStream_t stream);
+                         int max_k, int forced_len, int min_len, int max_chunks, int cu_count,
+                         float scale, void* out, float* lse, int32_t* hdr, int32_t* chunk_base,
+                         int32_t* recs, float* ws_o, float* ws_lse, hipStream_t stream);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const void* segs,
                             const int32_t* seg_indptr, const int32_t* cu_new, const int32_t* cu_k,
                             int batch, int total_new, int hkv, int64_t pool_tokens, int fmt,
@@ -122,6 +122,9 @@ DecodeWs decode_ws_layout(int64_t batch, int64_t hq, int64_t max_chunks) {
   return w;
 }
 
+// True when p is not a multiple of a (a power of two); NULL counts as aligned.
+bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
+
 seg_attn_status_t check_heads(int32_t hq, int32_t hkv, int32_t head_dim) {
   if (hq <= 0 || hkv <= 0 || head_dim <= 0) return SEG_ATTN_ERR_INVALID_ARG;
   if (hq % hkv != 0) return SEG_ATTN_ERR_INVALID_ARG;
@@ -166,6 +169,12 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
     if (batch == 0 || max_seqlen_q == 0) return SEG_ATTN_OK;
     if (!q || !k_pool || !v_pool || !segs || !seg_indptr || !cu_seqlens_q || !cu_seqlens_k || !out)
       return SEG_ATTN_ERR_INVALID_ARG;
+    // 16-byte loads and HBM->LDS copies of Q, K, V rows and 16-byte stores of output rows;
+    // 8-byte segment records; 4-byte table entries and LSE values
+    if (misaligned(q, 16) || misaligned(k_pool, 16) || misaligned(v_pool, 16) || misaligned(out, 16) ||
+        misaligned(segs, 8) || misaligned(seg_indptr, 4) || misaligned(cu_seqlens_q, 4) ||
+        misaligned(cu_seqlens_k, 4) || misaligned(lse, 4))
+      return SEG_ATTN_ERR_INVALID_ARG;
     const int64_t grid = ceil_div(max_seqlen_q, 16) * (int64_t)num_heads_kv * batch;
     if (grid > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
     hipError_t e = segattn::launch_prefill(q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_q,
@@ -207,6 +216,57 @@ size_t seg_attn_decode_workspace_bytes(int32_t batch, int32_t max_seqlen_k, int3
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Body of the decode entry point.
+seg_attn_status_t decode_impl(const void* q, const void* k_pool, const void* v_pool,
+                              const float* k_scale, const float* v_scale, int32_t kv_dtype,
+                              const seg_attn_segment_t* segs, const int32_t* seg_indptr,
+                              const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
+                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                              int64_t pool_tokens, float softmax_scale, int32_t num_splits, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  if (batch < 0 || max_seqlen_k < 0 || pool_tokens < 0 || num_splits < 0) return SEG_ATTN_ERR_INVALID_ARG;
+  if (!valid_kv_dtype(kv_dtype)) return SEG_ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return SEG_ATTN_ERR_INVALID_ARG;
+  seg_attn_status_t hs = check_heads(num_heads_q, num_heads_kv, head_dim);
+  if (hs != SEG_ATTN_OK) return hs;
+  if (pool_tokens > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
+  if (batch == 0) return SEG_ATTN_OK;
+  const bool scaled = kv_dtype != SEG_ATTN_KV_BF16;  // FP8 or INT8 codes with fp32 scales
+  if (!q || !k_pool || !v_pool || !segs || !seg_indptr || !cu_seqlens_k || !out) return SEG_ATTN_ERR_INVALID_ARG;
+  if (scaled && (!k_scale || !v_scale)) return SEG_ATTN_ERR_INVALID_ARG;
+  // 16-byte HBM->LDS copies of Q rows and pool rows, 4-byte scale copies, 8-byte output
+  // stores, 16-byte workspace records and partials
+  if (misaligned(q, 16) || misaligned(k_pool, 16) || misaligned(v_pool, 16) || misaligned(out, 8) ||
+      misaligned(segs, 8) || misaligned(seg_indptr, 4) || misaligned(cu_seqlens_k, 4) ||
+      misaligned(lse, 4) || (scaled && (misaligned(k_scale, 4) || misaligned(v_scale, 4))))
+    return SEG_ATTN_ERR_INVALID_ARG;
+  DecodePlan p;
+  if (!plan_decode(batch, max_seqlen_k, scaled, num_splits, &p)) return SEG_ATTN_ERR_INVALID_ARG;
+  int64_t max_chunks = p.per_request * batch;
+  int cu_count = 0;  // read from the device only once the call is going to launch
+  if (max_chunks * num_heads_kv > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
+  const DecodeWs lay = decode_ws_layout(batch, num_heads_q, max_chunks);
+  if (misaligned(workspace, 16)) return SEG_ATTN_ERR_WORKSPACE;
+  if (workspace == nullptr || workspace_bytes < lay.total) return SEG_ATTN_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  if (cu_count == 0) cu_count = current_cu_count();
+  hipError_t e = segattn::launch_decode(
+      q, k_pool, v_pool, k_scale, v_scale, kv_dtype, segs, seg_indptr, cu_seqlens_k, batch,
+      num_heads_kv, max_seqlen_k, p.forced_len, p.min_len, (int)max_chunks, cu_count, softmax_scale,
+      out, lse, (int32_t*)ws, (int32_t*)(ws + lay.base), (int32_t*)(ws + lay.tab), (float*)(ws + lay.o),
+      (float*)(ws + lay.lse), stream);
+  return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
 seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                                   const float* k_scale, const float* v_scale, int32_t kv_dtype,
                                   const seg_attn_segment_t* segs, const int32_t* seg_indptr,
@@ -216,29 +276,10 @@ seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void*
                                   int32_t num_splits, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, seg_attn_stream_t stream) {
   try {
-    if (batch < 0 || max_seqlen_k < 0 || pool_tokens < 0 || num_splits < 0) return SEG_ATTN_ERR_INVALID_ARG;
-    if (!valid_kv_dtype(kv_dtype)) return SEG_ATTN_ERR_INVALID_ARG;
-    if (!std::isfinite(softmax_scale)) return SEG_ATTN_ERR_INVALID_ARG;
-    seg_attn_status_t hs = check_heads(num_heads_q, num_heads_kv, head_dim);
-    if (hs != SEG_ATTN_OK) return hs;
-    if (pool_tokens > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
-    if (batch == 0) return SEG_ATTN_OK;
-    const bool scaled = kv_dtype != SEG_ATTN_KV_BF16;  // FP8 or INT8 codes with fp32 scales
-    if (!q || !k_pool || !v_pool || !segs || !seg_indptr || !cu_seqlens_k || !out) return SEG_ATTN_ERR_INVALID_ARG;
-    if (scaled && (!k_scale || !v_scale)) return SEG_ATTN_ERR_INVALID_ARG;
-    DecodePlan p;
-    if (!plan_decode(batch, max_seqlen_k, scaled, num_splits, &p)) return SEG_ATTN_ERR_INVALID_ARG;
-    const int64_t max_chunks = p.per_request * batch;
-    if (max_chunks * num_heads_kv > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
-    const DecodeWs lay = decode_ws_layout(batch, num_heads_q, max_chunks);
-    if (workspace == nullptr || workspace_bytes < lay.total) return SEG_ATTN_ERR_WORKSPACE;
-    char* ws = (char*)workspace;
-    hipError_t e = segattn::launch_decode(
-        q, k_pool, v_pool, k_scale, v_scale, kv_dtype, segs, seg_indptr, cu_seqlens_k, batch,
-        num_heads_kv, p.forced_len, p.min_len, (int)max_chunks, current_cu_count(), softmax_scale, out,
-        lse, (int32_t*)ws, (int32_t*)(ws + lay.base), (int32_t*)(ws + lay.tab), (float*)(ws + lay.o),
-        (float*)(ws + lay.lse), (hipStream_t)stream);
-    return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
+    return decode_impl(q, k_pool, v_pool, k_scale, v_scale, kv_dtype, segs, seg_indptr, cu_seqlens_k,
+                       batch, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, pool_tokens,
+                       softmax_scale, num_splits, out, lse, workspace, workspace_bytes,
+                       (hipStream_t)stream);
   } catch (...) {
     return SEG_ATTN_ERR_HIP;
   }
@@ -264,7 +305,6 @@ seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
       return SEG_ATTN_ERR_INVALID_ARG;
     if (scaled && (!k_scale || !v_scale)) return SEG_ATTN_ERR_INVALID_ARG;
     // rows move as 16-byte (bf16) or 8-byte (one-byte codes) pieces, scales as 4-byte words
-    auto misaligned = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
     if (misaligned(k_new, 16) || misaligned(v_new, 16) || misaligned(k_pool, scaled ? 8 : 16) ||
         misaligned(v_pool, scaled ? 8 : 16) || (scaled && (misaligned(k_scale, 4) || misaligned(v_scale, 4))))
       return SEG_ATTN_ERR_INVALID_ARG;
@@ -290,7 +330,6 @@ seg_attn_status_t check_linear(const void* q, const void* k, const void* v, cons
   if ((int64_t)batch * heads * 2 > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
   if (batch == 0) return SEG_ATTN_OK;
   if (!q || !k || !v || !g || !slots || !pool || !out) return SEG_ATTN_ERR_INVALID_ARG;
-  auto misaligned = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(pool, 16) ||
       misaligned(out, 8) || misaligned(g, 4))
     return SEG_ATTN_ERR_INVALID_ARG;

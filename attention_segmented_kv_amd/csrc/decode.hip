@@ -311,15 +311,17 @@ __device__ __forceinline__ void block_scan2(int& a, int& b, int* wtot) {
 // to its columns in snake order, which spreads the short chunks evenly. One thread per request;
 // the table reads are issued together (key counts, segment ranges, then the first segments) so
 // the plan costs few memory latencies.
-// hdr[0] = len, hdr[1] = number of chunks listed (0 if they would not fit in max_chunks).
+// hdr[0] = len, hdr[1] = number of chunks listed, hdr[2] = 1 when some K_b exceeds max_k (the
+// host's bound, which sized the workspace): then no chunk is listed and the merge pass writes
+// NaN to every output and LSE, so that the broken bound cannot pass unnoticed.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(
     const int32_t* __restrict__ cu_k, const int32_t* __restrict__ seg_indptr,
     const Segment* __restrict__ segs, int batch, int hkv, int forced_len, int min_len,
-    int target_units, int max_chunks, int32_t* __restrict__ hdr, int32_t* __restrict__ chunk_base,
-    int32_t* __restrict__ recs) {
+    int target_units, int max_chunks, int max_k, int32_t* __restrict__ hdr,
+    int32_t* __restrict__ chunk_base, int32_t* __restrict__ recs) {
   __shared__ int wtot[32];
   __shared__ int hist[kBuckets], bucket_base[kBuckets], bucket_fill[kBuckets];
-  __shared__ int carry_n, carry_f;
+  __shared__ int carry_n, carry_f, too_long;
   // batches of at most kSpreadMax requests: each request's scan results and first segments,
   // for the threads that share its chunks in pass 2
   __shared__ int rq_first[kSpreadMax], rq_ffirst[kSpreadMax], rq_n[kSpreadMax], rq_f[kSpreadMax];
@@ -361,6 +363,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
   if (tid == 0) {
     carry_n = 0;
     carry_f = 0;
+    too_long = 0;
   }
   __syncthreads();
   // pass 1: totals and the histogram of the short last chunks
@@ -369,6 +372,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
   for (int b0 = 0; b0 < batch; b0 += 1024) {
     const int b = b0 + tid;
     const int K = b0 == 0 ? K0 : (b < batch ? cu_k[b + 1] - cu_k[b] : 0);
+    if (K > max_k) too_long = 1;  // any writer stores the same value
     int n, f;
     counts(K, n, f);
     if (n > f) atomicAdd(&hist[(int)((int64_t)(K - f * len) * kBuckets / len)], 1);
@@ -511,8 +515,12 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
   if (tid == 0) {
     chunk_base[batch] = total_n;
     hdr[0] = len;
-    // more chunks than the workspace holds means some K_b exceeded max_seqlen_k: list none
-    hdr[1] = total_n <= max_chunks ? total_n : 0;
+    // a key count above the host's bound (which the workspace was sized for): list nothing and
+    // let the merge pass mark every output (the scan above ended in a barrier, so too_long is
+    // final)
+    const int bad = too_long != 0 || total_n > max_chunks;
+    hdr[1] = bad ? 0 : total_n;
+    hdr[2] = bad ? 1 : 0;
   }
 }
 
@@ -980,10 +988,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
   const int head = g * kGroup + (tid >> 5);
   const int d4 = (tid & 31) * 4;
   const int n_chunks = hdr[1];
+  const int64_t row = (int64_t)b * hq + head;
+  if (hdr[2] != 0) {
+    // the plan found a key count above max_seqlen_k: nothing was computed
+    const bf16_t nan_bf16 = (bf16_t)NAN;
+    *reinterpret_cast<bf16x4*>(out + row * kHeadDim + d4) = bf16x4{nan_bf16, nan_bf16, nan_bf16, nan_bf16};
+    if (lse != nullptr && (tid & 31) == 0) lse[row] = NAN;
+    return;
+  }
   const int c0 = chunk_base[b];
   const int c1 = min(chunk_base[b + 1], n_chunks);
   if (c1 - c0 == 1) return;
-  const int64_t row = (int64_t)b * hq + head;
   float M = -INFINITY;
   for (int c = c0 + (tid & 31); c < c1; c += 32) M = fmaxf(M, ws_lse[(int64_t)c * hq + head]);
 #pragma unroll
@@ -1032,17 +1047,17 @@ constexpr int kUnitsPerWorkgroup = 6;
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int kv, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,
-                         int forced_len, int min_len, int max_chunks, int cu_count, float scale,
-                         void* out, float* lse, int32_t* hdr, int32_t* chunk_base, int32_t* recs,
-                         float* ws_o, float* ws_lse, hipStream_t stream) {
+                         int max_k, int forced_len, int min_len, int max_chunks, int cu_count,
+                         float scale, void* out, float* lse, int32_t* hdr, int32_t* chunk_base,
+                         int32_t* recs, float* ws_o, float* ws_lse, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   // columns: one workgroup per (column, kv head), about one workgroup per compute unit
   const int cols = (int)std::max<int64_t>(1, std::min<int64_t>(cu_count / hkv, max_chunks));
   const int grid = max_chunks > 0 ? cols * hkv : 0;
   const int target = std::max(1, kUnitsPerWorkgroup * std::max(grid, 1));
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, cu_k, seg_indptr,
-                     (const Segment*)segs, batch, hkv, forced_len, min_len, target, max_chunks, hdr,
-                     chunk_base, recs);
+                     (const Segment*)segs, batch, hkv, forced_len, min_len, target, max_chunks, max_k,
+                     hdr, chunk_base, recs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (grid > 0) {

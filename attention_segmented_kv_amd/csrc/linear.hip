@@ -478,7 +478,7 @@ constexpr int kScanDepth = 8;
 __global__ __launch_bounds__(kLaThreads) void la_scan_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, int H, int maxc,
     int initial_state, float* __restrict__ pool, int64_t pool_slots, const float* __restrict__ ds,
-    const float* __restrict__ glast, uint16_t* __restrict__ sb) {
+    const float* __restrict__ glast, uint16_t* __restrict__ sb, uint16_t* __restrict__ out) {
   constexpr int kGroups = kLaDim / kScanCols;
   const int db = blockIdx.x % kGroups;
   const int bh = blockIdx.x / kGroups;
@@ -522,6 +522,15 @@ __global__ __launch_bounds__(kLaThreads) void la_scan_kernel(
         }
       }
     }
+  }
+  if (n > maxc * kChunk) {
+    // A request longer than max_seqlen, the host's bound that sized the workspace: its tokens
+    // past the bound are not computed. They and the final state get NaN (this workgroup's
+    // columns), so that the broken bound cannot pass unnoticed.
+    for (int t = maxc * kChunk + i4; t < n; t += 32)
+      out[((int64_t)cu[b] + t) * H * kLaDim + (int64_t)h * kLaDim + d] = 0x7FC0;  // bf16 NaN
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[e] = NAN;
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) sp[(4 * i4 + e) * kLaDim + d] = S[e];
@@ -656,7 +665,8 @@ hipError_t launch_linear_prefill_parallel(const void* q, const void* k, const vo
   }
   hipLaunchKernelGGL(la_scan_kernel, dim3((unsigned)((int64_t)batch * heads * (kLaDim / kScanCols))),
                      dim3(kLaThreads), 0,
-                     stream, cu, slots, heads, maxc, initial_state, pool, pool_slots, ds, gl, sb);
+                     stream, cu, slots, heads, maxc, initial_state, pool, pool_slots, ds, gl, sb,
+                     (uint16_t*)out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || chunk_grid == 0) return e;
   hipLaunchKernelGGL(la_chunk_out_kernel, dim3((unsigned)chunk_grid), dim3(kLaThreads), 0, stream,

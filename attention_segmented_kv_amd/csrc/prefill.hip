@@ -83,6 +83,24 @@ struct BlockCursor {
   }
 };
 
+// Query rows at or past position `first` of a request (q0: its first row) for the 8 heads of kv
+// head g. The grid covers positions below max_seqlen_q, the host's bound of every Lq_b; rows of
+// a request that breaks it are never computed, and the workgroup of the last query tile writes
+// NaN to them (and to their LSE) so that the broken bound cannot pass unnoticed.
+__device__ __forceinline__ void mark_uncovered_rows(bf16_t* out, float* lse, int64_t q0,
+                                                    int first, int lq, int hq, int g) {
+  const int64_t n = (int64_t)(lq - first) * kGroup * (kHeadDim / 8);  // 16-byte pieces
+  const bf16_t nanv = (bf16_t)NAN;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t r = i / (kGroup * (kHeadDim / 8));
+    const int hh = (int)(i / (kHeadDim / 8) % kGroup), c = (int)(i % (kHeadDim / 8));
+    const int64_t row = (q0 + first + r) * hq + g * kGroup + hh;
+    *reinterpret_cast<bf16x8*>(out + row * kHeadDim + 8 * c) =
+        bf16x8{nanv, nanv, nanv, nanv, nanv, nanv, nanv, nanv};
+    if (lse != nullptr && c == 0) lse[row] = NAN;
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Wide tiles: 256 rows (32 query positions x 8 heads) per workgroup. Group 0 owns positions
 // 0-15 of the tile, group 1 positions 16-31; both groups consume every K/V block (so each block
@@ -122,6 +140,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
   if (p0 >= lq) return;
   const int K = cu_k[b + 1] - cu_k[b];
   const int hq = hkv * kGroup;
+  if (qtile == n_qtiles - 1 && lq > n_qtiles * kWidePos)
+    mark_uncovered_rows(out, lse, q0, n_qtiles * kWidePos, lq, hq, g);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -452,6 +472,8 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
   const int p0 = qtile * kPosPerTile;
   if (p0 >= lq) return;
   const int hq = hkv * kGroup;
+  if (qtile == n_qtiles - 1 && lq > n_qtiles * kPosPerTile)
+    mark_uncovered_rows(out, lse, q0, n_qtiles * kPosPerTile, lq, hq, g);
   const int kfull = kCausal ? min(K, K - lq + p0 + 1) : K;  // keys every row sees
   const int tend = kCausal ? min(K, K - lq + min(p0 + kPosPerTile, lq)) : K;
   const int nblk = max(0, (tend + kBlockN - 1) / kBlockN);  // key blocks the tile sees

@@ -278,6 +278,41 @@ def time_steps(step, steps: int, warmup: int, graph: bool = False):
             "graph": 1.0 if graph else 0.0}
 
 
+def per_call_times(step, calls: int = 100):
+    """Per-call GPU durations: `calls` calls issued back to back, each bracketed by its own pair
+    of events on the launch stream. Returns the median and mean in microseconds. A call whose
+    host-side issue takes longer than the GPU work before it includes that idle gap."""
+    import statistics
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    return {"per_call_us_median": round(statistics.median(us), 3),
+            "per_call_us_mean": round(statistics.fmean(us), 3), "per_call_n": calls}
+
+
+def back_to_back(step, calls: int = 1000):
+    """`calls` calls between a single pair of events (no synchronisation in between): the
+    per-call time with launch gaps amortised."""
+    import torch
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(calls):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / calls, 3)
+
+
 def load_traffic(kind: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they were taken on
     the current kernel source; else None."""
@@ -293,35 +328,73 @@ def load_traffic(kind: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The oracle, as it stands, on the host cores: whole-workload passes of the prefill
-    workload repeated until about budget_s seconds have been spent."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
+# The oracle's sample per workload: (requests to evaluate, None = all; passes; how it is named).
+# Prefill samples take whole requests (every head and query row); decode samples whole requests
+# (every head). Sizes keep each sample at a few seconds to a few tens of seconds of host work.
+CPU_SAMPLES = {1: (None, 3), 2: (None, 3), 3: ([0], 1), 4: (None, 1), 5: ([0, 1], 1), 6: ([0, 1], 1)}
+
+
+def cpu_baseline(w, c: int):
+    """The oracle, as it stands, on the host cores, over a bounded sample of the workload (whole
+    requests), timed with perf_counter (best of the passes). Prefill: causal-adjusted TFLOP/s of
+    the sampled requests; decode: GB/s of the sampled requests' K/V (same algorithmic bytes as the
+    GPU figure)."""
     import numpy as np
     import oracle
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    reqs, passes = CPU_SAMPLES.get(c, (None, 1))
     segs, ind, cq, ck = wl.host_tables(w)
     qb, kb, vb = wl.bits(w.q), wl.bits(w.k_pool), wl.bits(w.v_pool)
-    passes, t_total = 0, 0.0
-    while t_total < budget_s and passes < 50:
+    ks = None if w.k_scale is None else w.k_scale.detach().cpu().numpy()
+    vs = None if w.v_scale is None else w.v_scale.detach().cpu().numpy()
+    best = float("inf")
+    for _ in range(passes):
         t0 = time.perf_counter()
         oracle.attention(qb, kb, vb, segs, ind, cq, ck, num_heads_kv=w.num_heads_kv,
-                         softmax_scale=w.softmax_scale, causal=w.causal)
-        t_total += time.perf_counter() - t0
-        passes += 1
-    tflops = prefill_flops(w) * passes / t_total / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the whole workload (all 64 heads x {int(w.q_lens.sum())} "
-                      f"query rows), float64 numpy, {t_total:.1f} s total"}
+                         softmax_scale=w.softmax_scale, causal=w.causal, kv_format=w.kv_dtype,
+                         k_scale=ks, v_scale=vs, requests=reqs)
+        best = min(best, time.perf_counter() - t0)
+    sel = list(range(w.batch)) if reqs is None else reqs
+    ql, kl = w.q_lens[sel], w.k_lens[sel]
+    if w.kind == "prefill":
+        pairs = sum(int(a) * (int(k) - int(a)) + int(a) * (int(a) + 1) // 2 if w.causal else int(a) * int(k)
+                    for a, k in zip(ql, kl))
+        value, unit = 4.0 * w.head_dim * w.num_heads_q * pairs / best / 1e12, "TFLOP/s"
+    else:
+        per_tok = w.num_heads_kv * w.head_dim * (2 if w.kv_dtype == "bf16" else 1) * 2
+        if w.kv_dtype != "bf16":
+            per_tok += w.num_heads_kv * 8
+        value, unit = float(kl.sum()) * per_tok / best / 1e9, "GB/s"
+    what = "the whole workload" if reqs is None else f"requests {reqs} of {w.batch} (every head)"
+    return {"value": value, "unit": unit, "cores": int(blas_threads()), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{what}, float64 numpy, best of {passes} pass(es): {best:.2f} s"}
 
 
-def measure(w, steps, warmup, kind, graph=False):
+def measure(w, steps, warmup, kind, graph=False, loop_1000=False):
     step = make_step(w)
     t = time_steps(step, steps, warmup, graph)
+    t.update(per_call_times(step))
+    if loop_1000:
+        t["back_to_back_1000_us"] = back_to_back(step, 1000)
     if kind == "prefill":
         work = prefill_flops(w)
         achieved = work / (t["launch_ms_mean"] * 1e-3) / 1e12
@@ -410,11 +483,12 @@ def main():
 
     head_c = args.config
     log(f"[bench] generating headline workload config {head_c}")
-    w_cpu = wl.make_config(head_c, device="cpu", poison=True) if head_c in (1, 2, 3) else None
-    w = w_cpu.to(dev) if w_cpu is not None else wl.make_config(head_c, device=dev)
+    w = wl.make_config(head_c, device="cpu", poison=True).to(dev) if head_c in (1, 2, 3) \
+        else wl.make_config(head_c, device=dev)
     kind = w.kind
     log(f"[bench] timing {w.name}: warmup {args.warmup}, steps {args.steps}")
-    value, unit, roof, t, work = measure(w, args.steps, args.warmup, kind, args.graph)
+    value, unit, roof, t, work = measure(w, args.steps, args.warmup, kind, args.graph,
+                                         loop_1000=head_c in (1, 2))
     log(f"[bench] {w.name}: {value:.2f} {unit} per step, launch mean {t['launch_ms_mean']*1e3:.1f} us, "
         f"roofline frac {roof['frac']:.3f}")
 
@@ -447,11 +521,20 @@ def main():
                 continue
             log(f"[bench] config {c}: generating")
             wc = wl.make_config(c, device=dev)
-            v, u, rf, tc, wk = measure(wc, max(20, args.steps // 2), args.warmup, wc.kind, args.graph)
-            log(f"[bench] {wc.name}: {v:.2f} {u}, launch mean {tc['launch_ms_mean']*1e3:.1f} us, frac {rf['frac']:.3f}")
-            extra.append({"workload": wc.name, "value": round(v, 3), "unit": u,
-                          "launch_us_mean": round(tc["launch_ms_mean"] * 1e3, 2),
-                          "roofline": rf, "work_per_step": wk})
+            v, u, rf, tc, wk = measure(wc, max(20, args.steps // 2), args.warmup, wc.kind, args.graph,
+                                       loop_1000=c in (1, 2))
+            log(f"[bench] {wc.name}: {v:.2f} {u}, launch mean {tc['launch_ms_mean']*1e3:.1f} us, "
+                f"per-call median {tc['per_call_us_median']:.1f} us, frac {rf['frac']:.3f}")
+            entry = {"workload": wc.name, "value": round(v, 3), "unit": u,
+                     "launch_us_mean": round(tc["launch_ms_mean"] * 1e3, 2),
+                     "timing": {k: round(x, 6) for k, x in tc.items()},
+                     "roofline": rf, "work_per_step": wk}
+            if not args.no_cpu_baseline:
+                log(f"[bench] {wc.name}: cpu baseline (oracle)")
+                entry["cpu_baseline"] = cpu_baseline(wc, c)
+                log(f"[bench] {wc.name}: oracle {entry['cpu_baseline']['value']:.4g} "
+                    f"{entry['cpu_baseline']['unit']} ({entry['cpu_baseline']['sample']})")
+            extra.append(entry)
             del wc
             torch.cuda.empty_cache()
         result["configs"] = extra
@@ -480,8 +563,8 @@ def main():
 
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        wb = w_cpu if w_cpu is not None else wl.make_config(2, device="cpu")
-        result["cpu_baseline"] = cpu_baseline(wb)
+        result["cpu_baseline"] = cpu_baseline(w, head_c)
+        log(f"[bench] {w.name}: oracle {result['cpu_baseline']['value']:.4g} {result['cpu_baseline']['unit']}")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -85,12 +85,20 @@ enum { SEG_ATTN_KV_BF16 = 0, SEG_ATTN_KV_FP8_E4M3 = 1, SEG_ATTN_KV_INT8 = 2 };
  * q            [total_q, Hq, 128] bf16, total_q = cu_seqlens_q[batch].
  * k_pool/v_pool[pool_tokens, Hkv, 128] bf16.
  * segs, seg_indptr, cu_seqlens_q, cu_seqlens_k: as in the header comment (device).
- * max_seqlen_q, max_seqlen_k: HOST upper bounds of Lq_b and K_b (they size the launch grid;
- *              rows beyond a request's real length are skipped).
+ * max_seqlen_q: HOST upper bound of every Lq_b; it sizes the launch grid. Query rows at
+ *              positions >= the grid's coverage (ceil(max_seqlen_q / tile) * tile, tile 16 or 32)
+ *              of a request that breaks the bound are not computed: they and their LSE are
+ *              written as NaN, so the broken bound shows in the output.
+ * max_seqlen_k: HOST upper bound of every K_b; with causal, max_seqlen_q <= max_seqlen_k is
+ *              required (INVALID_ARG otherwise). The kernels do not depend on it otherwise.
  * softmax_scale: multiplies Q K^T (1/sqrt(128) for the usual scaling).
- * causal:      0 or 1. With causal, Lq_b > K_b is invalid (not checked on the device).
- * out          [total_q, Hq, 128] bf16, written for every query row of every request.
+ * causal:      0 or 1. With causal and Lq_b > K_b the first Lq_b - K_b rows of request b see no
+ *              key (seg_attn_validate_tables reports such tables).
+ * out          [total_q, Hq, 128] bf16, written for every query row of every request; a row
+ *              that sees no key gets 0 (and LSE -inf).
  * lse          [total_q, Hq] fp32 or NULL.
+ * Alignment:   q, k_pool, v_pool and out 16 bytes; segs 8; the tables and lse 4
+ *              (SEG_ATTN_ERR_INVALID_ARG otherwise); torch and hipMalloc allocations are.
  * Returns SEG_ATTN_OK, or an error before anything is launched.
  */
 seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
@@ -110,7 +118,9 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
  * k_scale/v_scale [pool_tokens, Hkv] fp32 for FP8 and INT8 (required), ignored (may be NULL)
  *              for bf16. Codes are converted to bf16 exactly; k_scale multiplies the fp32
  *              scores and v_scale the fp32 probabilities before their bf16 rounding.
- * cu_seqlens_k [batch+1] int32; max_seqlen_k: HOST upper bound of K_b.
+ * cu_seqlens_k [batch+1] int32; max_seqlen_k: HOST upper bound of every K_b; it sizes the
+ *              workspace. If some K_b exceeds it, nothing is computed and every output and
+ *              LSE of the call is written as NaN, so the broken bound shows in the output.
  * num_splits   0: each request's keys are cut into chunks whose length the device picks from the
  *              total key count (at least 512 keys for bf16, 1024 for fp8 / int8) so that every compute
  *              unit gets several (chunk, kv head) work units. n > 0: chunks of
@@ -123,6 +133,8 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
  *              same (batch, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, kv_dtype,
  *              num_splits); always required. It holds the chunk plan and the partial results;
  *              its contents need no initialisation and are clobbered.
+ * Alignment:   q, k_pool and v_pool 16 bytes, out 8, segs 8, tables, scales and lse 4
+ *              (SEG_ATTN_ERR_INVALID_ARG otherwise); workspace 16 (SEG_ATTN_ERR_WORKSPACE).
  */
 seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                                   const float* k_scale, const float* v_scale, int32_t kv_dtype,
@@ -207,7 +219,8 @@ seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
  * fp32 state. With a workspace (of seg_attn_linear_prefill_workspace_bytes(batch, max_seqlen,
  * H, 128) bytes, 256-byte aligned, contents clobbered) all chunks of all requests run in
  * parallel, with a scan carrying the state between them; max_seqlen (HOST) must be at least every
- * request's length (longer requests are not processed past it). With workspace = NULL one
+ * request's length: a longer request is not processed past it, and its later tokens' outputs and
+ * its final state are written as NaN so the broken bound shows. With workspace = NULL one
  * workgroup per (request, head, half of d_v) walks the chunks in order and max_seqlen is unused. Decode: one token per request (row b), state read from and written to the slot,
  * in fp32 throughout. Buffers: q, k, v and the pool 16-byte aligned, out 8-byte.
  * Returns SEG_ATTN_OK, or an error before anything is launched.

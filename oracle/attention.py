@@ -72,13 +72,18 @@ def int8_to_f64(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits).astype(np.uint8).view(np.int8).astype(np.float64)
 
 
+# The 256 E4M3FN codes decoded once by the definition above; decoding a pool is then a table
+# lookup with the same values (the definition's arithmetic per element is slow on long pools).
+_E4M3FN_VALUES = e4m3fn_to_f64(np.arange(256))
+
+
 def decode_kv(bits: np.ndarray, scale: Optional[np.ndarray], fmt: str) -> np.ndarray:
     """Decoded K or V rows [n, Hkv, D] in float64. For FP8 and INT8 the code is multiplied by
     its per-(token, kv head) fp32 scale; the product of two such numbers is exact in float64."""
     if fmt == "bf16":
         return bf16_to_f64(bits)
     if fmt == "fp8_e4m3":
-        return e4m3fn_to_f64(bits) * np.asarray(scale, dtype=np.float64)[..., None]
+        return _E4M3FN_VALUES[np.asarray(bits).astype(np.uint8)] * np.asarray(scale, dtype=np.float64)[..., None]
     if fmt == "int8":
         return int8_to_f64(bits) * np.asarray(scale, dtype=np.float64)[..., None]
     raise ValueError(f"unknown kv format {fmt}")

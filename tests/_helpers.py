@@ -52,26 +52,6 @@ def oracle_rows(w: wl.Workload, rows, h=None):
                                  kv_format=w.kv_dtype, k_scale=h["k_scale"], v_scale=h["v_scale"])
 
 
-def sample_rows(w: wl.Workload, n: int, seed: int = 0):
-    """n (request, query index, head) rows: each request's first and last query row plus
-    uniform random ones, spread over all heads."""
-    rng = np.random.default_rng(seed)
-    rows = []
-    hq = w.num_heads_q
-    for b in range(w.batch):
-        lq = int(w.q_lens[b])
-        if lq == 0:
-            continue
-        rows.append((b, 0, int(rng.integers(hq))))
-        rows.append((b, lq - 1, int(rng.integers(hq))))
-    while len(rows) < n:
-        b = int(rng.integers(w.batch))
-        lq = int(w.q_lens[b])
-        if lq:
-            rows.append((b, int(rng.integers(lq)), int(rng.integers(hq))))
-    return rows
-
-
 def errors(got: np.ndarray, ref: np.ndarray):
     d = got.astype(np.float64) - ref
     return float(np.abs(d).max(initial=0.0)), float(math.sqrt(np.mean(d * d))) if d.size else 0.0
@@ -92,10 +72,3 @@ def assert_lse_close(got, ref, what=""):
     if (~inf_ref).any():
         err = np.abs(got[~inf_ref] - ref[~inf_ref]).max()
         assert err <= LSE_TOL, f"{what}: LSE max abs err {err:.3e}"
-
-
-def gather_rows(out: torch.Tensor, w: wl.Workload, rows):
-    cq = w.cu_seqlens_q.cpu().numpy()
-    idx_t = torch.tensor([int(cq[b]) + i for b, i, _ in rows], device=out.device)
-    idx_h = torch.tensor([h for _, _, h in rows], device=out.device)
-    return out[idx_t, idx_h].float().cpu().numpy()

@@ -50,8 +50,10 @@ def test_status_strings():
 
 
 def _prefill_args(**over):
-    a = dict(q=1, k=1, v=1, segs=1, ind=1, cq=1, ck=1, batch=1, mq=4, mk=4, hq=64, hkv=8, d=128,
-             pool=16, scale=0.1, causal=1, out=1, lse=None, stream=None)
+    # nonzero, suitably aligned stand-ins for device pointers: every case is rejected (or is a
+    # no-op) before anything is launched
+    a = dict(q=256, k=256, v=256, segs=8, ind=4, cq=4, ck=4, batch=1, mq=4, mk=4, hq=64, hkv=8, d=128,
+             pool=16, scale=0.1, causal=1, out=256, lse=None, stream=None)
     a.update(over)
     return [a[k] for k in ("q", "k", "v", "segs", "ind", "cq", "ck", "batch", "mq", "mk", "hq", "hkv",
                            "d", "pool", "scale", "causal", "out", "lse", "stream")]
@@ -67,14 +69,26 @@ def test_prefill_rejects_bad_arguments(over, status):
     assert lib.seg_attn_prefill(*_prefill_args(**over)) == status
 
 
+@pytest.mark.parametrize("over", [
+    dict(q=264), dict(k=258), dict(v=260), dict(out=264), dict(segs=12), dict(ind=6), dict(cq=2),
+    dict(ck=3), dict(lse=6), dict(q=256 + 8, lse=4),
+])
+def test_prefill_rejects_misaligned_buffers(over):
+    """Q, K/V pool and output rows move as 16-byte pieces, segment records are 8 bytes, table
+    entries and LSE values 4 bytes: a pointer that breaks its alignment is rejected."""
+    lib = _lib()
+    assert lib.seg_attn_prefill(*_prefill_args(**over)) == 1
+
+
 def test_prefill_empty_batch_is_a_noop():
     lib = _lib()
     assert lib.seg_attn_prefill(*_prefill_args(batch=0, q=None, out=None)) == 0
 
 
 def _decode_args(**over):
-    a = dict(q=1, k=1, v=1, ks=None, vs=None, kvd=0, segs=1, ind=1, ck=1, batch=2, mk=100, hq=64,
-             hkv=8, d=128, pool=16, scale=0.1, ns=1, out=1, lse=None, ws=None, wsb=0, stream=None)
+    a = dict(q=256, k=256, v=256, ks=None, vs=None, kvd=0, segs=8, ind=4, ck=4, batch=2, mk=100,
+             hq=64, hkv=8, d=128, pool=16, scale=0.1, ns=1, out=256, lse=None, ws=None, wsb=0,
+             stream=None)
     a.update(over)
     return [a[k] for k in ("q", "k", "v", "ks", "vs", "kvd", "segs", "ind", "ck", "batch", "mk", "hq",
                            "hkv", "d", "pool", "scale", "ns", "out", "lse", "ws", "wsb", "stream")]
@@ -86,6 +100,19 @@ def _decode_args(**over):
     (dict(ns=0), 3), (dict(ns=1), 3), (dict(kvd=2), 1), (dict(kvd=2, vs=1), 1), (dict(kvd=3), 1),
 ])
 def test_decode_rejects_bad_arguments(over, status):
+    lib = _lib()
+    assert lib.seg_attn_decode(*_decode_args(**over)) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=264), 1), (dict(k=260), 1), (dict(v=257), 1), (dict(out=260), 1), (dict(segs=4), 1),
+    (dict(ck=2), 1), (dict(lse=2), 1), (dict(kvd=1, ks=2, vs=4), 1), (dict(kvd=2, ks=4, vs=6), 1),
+    (dict(kvd=1, k=256 + 8, ks=4, vs=4), 1), (dict(ws=264, wsb=1 << 40), 3),
+])
+def test_decode_rejects_misaligned_buffers(over, status):
+    """Q and pool rows are copied as 16-byte pieces, scales as 4-byte words, the output is
+    written 8 bytes at a time and the workspace holds 16-byte records: a pointer that breaks its
+    alignment is rejected (a misaligned workspace as a workspace error)."""
     lib = _lib()
     assert lib.seg_attn_decode(*_decode_args(**over)) == status
 
@@ -206,3 +233,4 @@ def test_validate_tables_accepts_good_and_flags_bad():
     cq2 = np.array([0, 2, 7, 12])
     assert sa.validate_tables(segs, ind, ck, w.pool_tokens, cu_seqlens_q=cq2) == (5, 2)
     assert sa.validate_tables(segs, ind, ck, w.pool_tokens, cu_seqlens_q=cq2, causal=False)[0] == 0
+

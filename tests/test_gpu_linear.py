@@ -166,3 +166,26 @@ def test_linear_prefill_is_deterministic(parallel):
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(p1.view(torch.int32), w.state_pool.view(torch.int32))
+
+
+@needs_gpu
+def test_linear_prefill_tokens_above_max_seqlen_give_nan():
+    """max_seqlen sizes the chunk-parallel workspace: tokens of a longer request past it and that
+    request's final state are NaN, the tokens before it are still correct."""
+    print("[case] linear prefill with a length above max_seqlen", flush=True)
+    sa = _sa()
+    w = wl.make_linear(37, [70, 40, 129], kind="prefill", initial_state=True, num_heads=4).to("cuda")
+    pool_before = w.state_pool.detach().cpu().clone()
+    o_ref, st_ref = _oracle(w, pool_before)
+    out = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool,
+                            initial_state=True, scale=w.scale, max_seqlen=64)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    bad = np.zeros(239, dtype=bool)
+    bad[64:70] = True
+    bad[110 + 64:239] = True
+    assert np.isnan(got[bad]).all()
+    _assert_rel(got[~bad], o_ref[~bad], "linear-bound")
+    st = w.state_pool.detach().cpu()[w.state_slots.long().cpu()].double().numpy()
+    assert np.isnan(st[0]).all() and np.isnan(st[2]).all()
+    assert np.abs(st[1] - st_ref[1]).max() <= STATE_REL * np.abs(st_ref[1]).max()

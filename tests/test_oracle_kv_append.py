@@ -78,6 +78,86 @@ def test_quantize_rows_scale_extremes_and_zero_rows():
     assert np.all(np.abs(dec - x) <= scale[..., None].astype(np.float64) * 16.0 * (1 + 1e-6))
 
 
+def _torch_fp8_rows(x: np.ndarray):
+    """torch's own fp32 division, clamp and float8_e4m3fn cast (round to nearest, ties to even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    amax = t.abs().amax(dim=-1)
+    sc = torch.where(amax > 0, amax / torch.tensor(448.0), torch.ones_like(amax))
+    q = (t / sc.unsqueeze(-1)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy(), sc.numpy()
+
+
+def _positive_bf16_values() -> np.ndarray:
+    """Every positive normal bf16 value, as float32."""
+    return (np.arange(0x0080, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+
+
+def _crafted_fp8_rows():
+    """Rows [amax, x, 0, ...] of bf16 values chosen so that the fp32 quotient x / s (s = amax/448)
+    decides the code where plausible mistakes decide it differently:
+      * 'tie' rows: fl32(x / s) is exactly the midpoint of two adjacent codes while the exact
+        quotient is not, so rounding the exact (fp64) quotient straight to a code differs from
+        ties-to-even on the fp32 quotient whenever the even code lies on the other side;
+      * 'recip' rows: x * fl32(1 / s) rounds to another code than x / s."""
+    xs_all = _positive_bf16_values()
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    v = oracle.e4m3fn_to_f64(codes)
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    tie, recip = [], []
+    for amax in xs_all[(xs_all >= 0.01) & (xs_all <= 1000.0)][::7]:
+        s = np.float32(amax / np.float32(448))
+        xs = xs_all[xs_all < amax]
+        q32 = xs / s
+        on_mid = np.isin(q32, mids) & (xs.astype(np.float64) / np.float64(s) != q32)
+        tie += [(amax, x) for x in xs[on_mid][:2]]
+        qr = xs * np.float32(np.float32(1) / s)
+        diff = oracle.f32_to_e4m3fn(np.minimum(qr, 448)) != oracle.f32_to_e4m3fn(np.minimum(q32, 448))
+        recip += [(amax, x) for x in xs[diff][:2]]
+    rows = np.zeros((len(tie) + len(recip), 128), dtype=np.float32)
+    for i, (a, x) in enumerate(tie + recip):
+        rows[i, 0], rows[i, 1] = a, x
+        rows[i, 2], rows[i, 3] = -a, -x  # the negative twins take the mirrored codes
+    return rows, len(tie), len(recip)
+
+
+def _nearest_code_f64(q: np.ndarray) -> np.ndarray:
+    """Mutant encoder for the pin below: the code nearest to an fp64 value (no fp32 step)."""
+    pos = np.arange(0, 0x7F, dtype=np.uint8)
+    v = oracle.e4m3fn_to_f64(pos)
+    a = np.abs(q)
+    idx = np.abs(a[..., None] - v).argmin(axis=-1)
+    return (pos[idx] | (np.signbit(q).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def test_fp8_quantiser_matches_torch_and_catches_plausible_mistakes():
+    """The FP8 row quantiser (the reading of the KV append: s = fl32(amax / 448) and codes
+    E4M3FN(clamp(x / s, +-448)) from a correctly rounded fp32 quotient, ties to even) against
+    torch's own division and float8 cast: random bf16 rows over many magnitudes, plus crafted
+    rows on which dividing in fp64 and rounding once, or multiplying by the reciprocal, give
+    other codes (checked below, so the pin would see either mistake)."""
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal((300, 8, 128)),
+                        rng.standard_normal((40, 8, 128)) * 1e-30,
+                        rng.uniform(-1e4, 1e4, (40, 8, 128))]).astype(np.float32)
+    x = oracle.bf16_bits_to_f32((x.view(np.uint32) >> 16).astype(np.uint16))  # bf16 values
+    codes, scale = oracle.quantize_rows(x)
+    tc, ts = _torch_fp8_rows(x)
+    assert np.array_equal(scale, ts) and np.array_equal(codes, tc)
+
+    rows, n_tie, n_recip = _crafted_fp8_rows()
+    assert n_tie >= 20 and n_recip >= 20
+    codes, scale = oracle.quantize_rows(rows)
+    tc, ts = _torch_fp8_rows(rows)
+    assert np.array_equal(scale, ts) and np.array_equal(codes, tc)
+    s = scale[:, None]
+    # mutant 1: the exact quotient rounded straight to a code
+    m1 = _nearest_code_f64(np.clip(rows.astype(np.float64) / s.astype(np.float64), -448, 448))
+    assert (m1[:n_tie] != tc[:n_tie]).any(axis=1).sum() >= n_tie // 4
+    # mutant 2: multiply by the fp32 reciprocal of the scale
+    m2 = oracle.f32_to_e4m3fn(np.clip(rows * (np.float32(1) / s).astype(np.float32), -448, 448))
+    assert (m2[n_tie:] != tc[n_tie:]).any(axis=1).all()
+
+
 def _torch_int8_rows(x: np.ndarray):
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     amax = t.abs().amax(dim=-1)
