@@ -22,7 +22,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "decode", "kv_append", "linear_prefill", "linear_decode", "SegmentAllocator",
+__all__ = ["prefill", "decode", "decode_noalloc", "kv_append", "linear_prefill", "linear_decode", "SegmentAllocator",
            "decode_num_splits", "decode_workspace_bytes", "validate_tables",
            "status_string", "version", "library_path", "SegAttnError", "KV_BF16", "KV_FP8_E4M3",
            "KV_INT8"]
@@ -62,6 +62,9 @@ def _load():
     lib.seg_attn_decode.argtypes = [P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, I64, F32, I32,
                                     P, P, P, SZ, P]
     lib.seg_attn_decode.restype = I32
+    lib.seg_attn_decode_noalloc.argtypes = [P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, I64, F32,
+                                            I32, P, P, P]
+    lib.seg_attn_decode_noalloc.restype = I32
     lib.seg_attn_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     lib.seg_attn_decode_workspace_bytes.restype = SZ
     lib.seg_attn_decode_num_splits.argtypes = [I32, I32, I32, I32, I32, ctypes.POINTER(I32)]
@@ -231,7 +234,7 @@ def decode_workspace_bytes(batch: int, max_seqlen_k: int, num_heads_q: int = 64,
 
 def _decode_args(q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_k, k_scale, v_scale, softmax_scale,
                  out, lse, return_lse):
-    """Argument checks of decode; allocates out / lse when not given."""
+    """Argument checks shared by decode and decode_noalloc; allocates out / lse when not given."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("q must be a GPU tensor")
@@ -304,6 +307,32 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: to
                                  _ptr(workspace), ws_bytes, stream)
     if st != 0:
         raise SegAttnError("seg_attn_decode", st)
+    return (out, lse) if return_lse else out
+
+
+def decode_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Tensor,
+                   seg_indptr: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_k: int, *,
+                   k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                   softmax_scale: Optional[float] = None, num_splits: int = 0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   return_lse: bool = False):
+    """decode() through seg_attn_decode_noalloc: no workspace; the library's fixed per-GPU
+    scratch holds the plan and partials (calls that overlap in time on one GPU race). With out
+    (and lse, if wanted) given, nothing is allocated on the device."""
+    lib = _load()
+    dev, kv_dtype, batch, hq, hkv, d, pool_tokens, scale, out, lse = _decode_args(
+        q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_k, k_scale, v_scale, softmax_scale, out, lse,
+        return_lse)
+    scaled = kv_dtype != KV_BF16
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.seg_attn_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                         _ptr(k_scale if scaled else None), _ptr(v_scale if scaled else None),
+                                         kv_dtype, _ptr(segs), _ptr(seg_indptr), _ptr(cu_seqlens_k), batch,
+                                         int(max_seqlen_k), hq, hkv, d, pool_tokens, scale,
+                                         int(num_splits), _ptr(out), _ptr(lse), stream)
+    if st != 0:
+        raise SegAttnError("seg_attn_decode_noalloc", st)
     return (out, lse) if return_lse else out
 
 

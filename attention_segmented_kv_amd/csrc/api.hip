@@ -34,6 +34,7 @@ hipError_t launch_linear_decode(const void* q, const void* k, const void* v, con
                                 const int32_t* slots, int batch, int heads, float scale, float* pool,
                                 int64_t pool_slots, void* out, hipStream_t stream);
 size_t linear_prefill_ws(int64_t batch, int64_t maxc, int64_t heads, size_t* off);
+int64_t decode_auto_chunk_bound(int64_t batch, int hkv, int cu_count);
 hipError_t launch_linear_prefill_parallel(const void* q, const void* k, const void* v, const float* g,
                                           const int32_t* cu, const int32_t* slots, int batch, int heads,
                                           int maxc, float scale, int initial_state, float* pool,
@@ -145,6 +146,7 @@ const char* seg_attn_status_string(seg_attn_status_t status) {
     case SEG_ATTN_ERR_HIP: return "HIP runtime error at launch";
     case SEG_ATTN_ERR_TABLE: return "inconsistent segment / length tables";
     case SEG_ATTN_ERR_OUT_OF_MEMORY: return "not enough free pool slots (or host memory)";
+    case SEG_ATTN_ERR_SCRATCH: return "call needs more than the fixed scratch of seg_attn_decode_noalloc";
     default: return "unknown status";
   }
 }
@@ -220,14 +222,43 @@ size_t seg_attn_decode_workspace_bytes(int32_t batch, int32_t max_seqlen_k, int3
 
 namespace {
 
-// Body of the decode entry point.
+// Scratch of seg_attn_decode_noalloc: the decode workspace (plan and partial results) in a
+// fixed array of every GPU the library runs on, held until the process ends. Host code never
+// uses the array's name as an address (in host code it is only a stand-in): its device address
+// is looked up once per device, with that device current, and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of the current device's scratch array (nullptr and the HIP error on failure).
+void* current_scratch(hipError_t* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
+// Shared body of the two decode entry points. noalloc: the workspace is the scratch array and
+// the automatic plan's chunk count is bounded by decode_auto_chunk_bound instead of the per-request
+// worst case, which keeps it small.
 seg_attn_status_t decode_impl(const void* q, const void* k_pool, const void* v_pool,
                               const float* k_scale, const float* v_scale, int32_t kv_dtype,
                               const seg_attn_segment_t* segs, const int32_t* seg_indptr,
                               const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_k,
                               int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                               int64_t pool_tokens, float softmax_scale, int32_t num_splits, void* out,
-                              float* lse, void* workspace, size_t workspace_bytes,
+                              float* lse, void* workspace, size_t workspace_bytes, bool noalloc,
                               hipStream_t stream) {
   if (batch < 0 || max_seqlen_k < 0 || pool_tokens < 0 || num_splits < 0) return SEG_ATTN_ERR_INVALID_ARG;
   if (!valid_kv_dtype(kv_dtype)) return SEG_ATTN_ERR_INVALID_ARG;
@@ -249,8 +280,19 @@ seg_attn_status_t decode_impl(const void* q, const void* k_pool, const void* v_p
   if (!plan_decode(batch, max_seqlen_k, scaled, num_splits, &p)) return SEG_ATTN_ERR_INVALID_ARG;
   int64_t max_chunks = p.per_request * batch;
   int cu_count = 0;  // read from the device only once the call is going to launch
+  if (noalloc && num_splits == 0) {
+    cu_count = current_cu_count();
+    max_chunks = std::min<int64_t>(max_chunks, segattn::decode_auto_chunk_bound(batch, num_heads_kv, cu_count));
+  }
   if (max_chunks * num_heads_kv > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
   const DecodeWs lay = decode_ws_layout(batch, num_heads_q, max_chunks);
+  if (noalloc) {
+    if (lay.total > kScratchBytes) return SEG_ATTN_ERR_SCRATCH;
+    hipError_t e = hipSuccess;
+    workspace = current_scratch(&e);
+    if (workspace == nullptr) return SEG_ATTN_ERR_HIP;
+    workspace_bytes = kScratchBytes;
+  }
   if (misaligned(workspace, 16)) return SEG_ATTN_ERR_WORKSPACE;
   if (workspace == nullptr || workspace_bytes < lay.total) return SEG_ATTN_ERR_WORKSPACE;
   char* ws = (char*)workspace;
@@ -278,8 +320,26 @@ seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void*
   try {
     return decode_impl(q, k_pool, v_pool, k_scale, v_scale, kv_dtype, segs, seg_indptr, cu_seqlens_k,
                        batch, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, pool_tokens,
-                       softmax_scale, num_splits, out, lse, workspace, workspace_bytes,
+                       softmax_scale, num_splits, out, lse, workspace, workspace_bytes, false,
                        (hipStream_t)stream);
+  } catch (...) {
+    return SEG_ATTN_ERR_HIP;
+  }
+}
+
+seg_attn_status_t seg_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                          const float* k_scale, const float* v_scale,
+                                          int32_t kv_dtype, const seg_attn_segment_t* segs,
+                                          const int32_t* seg_indptr, const int32_t* cu_seqlens_k,
+                                          int32_t batch, int32_t max_seqlen_k, int32_t num_heads_q,
+                                          int32_t num_heads_kv, int32_t head_dim,
+                                          int64_t pool_tokens, float softmax_scale,
+                                          int32_t num_splits, void* out, float* lse,
+                                          seg_attn_stream_t stream) {
+  try {
+    return decode_impl(q, k_pool, v_pool, k_scale, v_scale, kv_dtype, segs, seg_indptr, cu_seqlens_k,
+                       batch, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, pool_tokens,
+                       softmax_scale, num_splits, out, lse, nullptr, 0, true, (hipStream_t)stream);
   } catch (...) {
     return SEG_ATTN_ERR_HIP;
   }

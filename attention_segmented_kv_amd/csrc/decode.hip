@@ -1044,6 +1044,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
 // more pay for the extra partial results and merge work.
 constexpr int kUnitsPerWorkgroup = 6;
 
+// An upper bound of the chunks the automatic plan lists (num_splits = 0), whatever the key
+// counts: the length it picks is at least total * hkv / target, target = kUnitsPerWorkgroup *
+// grid, grid = columns * hkv with at most max(1, cu_count / hkv) columns, so the whole chunks
+// number at most kUnitsPerWorkgroup * columns and each request adds at most one short chunk;
+// at the 2^30 length cap a request of fewer than 2^31 keys has at most two chunks.
+int64_t decode_auto_chunk_bound(int64_t batch, int hkv, int cu_count) {
+  const int64_t cols = std::max(1, cu_count / std::max(1, hkv));
+  return kUnitsPerWorkgroup * cols + 2 * batch;
+}
+
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int kv, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,

@@ -71,7 +71,8 @@ enum {
   SEG_ATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
   SEG_ATTN_ERR_HIP = 4,         /* the HIP runtime reported an error at launch */
   SEG_ATTN_ERR_TABLE = 5,       /* seg_attn_validate_tables found an inconsistent table */
-  SEG_ATTN_ERR_OUT_OF_MEMORY = 6 /* the allocator's pool (or the host heap) cannot hold it */
+  SEG_ATTN_ERR_OUT_OF_MEMORY = 6, /* the allocator's pool (or the host heap) cannot hold it */
+  SEG_ATTN_ERR_SCRATCH = 7        /* seg_attn_decode_noalloc: more than its fixed scratch holds */
 };
 
 /* KV pool formats. FP8 and INT8 pools hold one-byte codes plus one fp32 scale per (token, kv
@@ -144,6 +145,30 @@ seg_attn_status_t seg_attn_decode(const void* q, const void* k_pool, const void*
                                   int32_t head_dim, int64_t pool_tokens, float softmax_scale,
                                   int32_t num_splits, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, seg_attn_stream_t stream);
+
+/*
+ * Decode without any allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The same computation and
+ * arguments as seg_attn_decode without the workspace: the plan and partial results live in a
+ * fixed scratch array of 64 MiB that the library keeps on every GPU it runs on until the process
+ * ends (its address is looked up on the first call on a device). The call allocates nothing.
+ * With num_splits = 0 the plan needs at most (6 * max(1, CUs / Hkv) + 2 * batch) chunks, with
+ * num_splits = n at most n * batch; each chunk takes Hq * 129 * 4 + 64 bytes (33 088 for
+ * Hq = 64), so 64 MiB holds about 2000 chunks (batch <= about 900 at Hq = 64 with automatic
+ * splits). A call that needs more returns SEG_ATTN_ERR_SCRATCH before anything is launched.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time on one GPU (on
+ * different streams, or from several host threads) race and must be serialised by the caller.
+ * Every part of the scratch a call reads is written earlier in the same call.
+ */
+seg_attn_status_t seg_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                          const float* k_scale, const float* v_scale,
+                                          int32_t kv_dtype, const seg_attn_segment_t* segs,
+                                          const int32_t* seg_indptr, const int32_t* cu_seqlens_k,
+                                          int32_t batch, int32_t max_seqlen_k, int32_t num_heads_q,
+                                          int32_t num_heads_kv, int32_t head_dim,
+                                          int64_t pool_tokens, float softmax_scale,
+                                          int32_t num_splits, void* out, float* lse,
+                                          seg_attn_stream_t stream);
 
 /* Bytes of workspace seg_attn_decode needs for these arguments: a 256-byte plan header, the
  * per-request chunk offsets, a 64-byte record per chunk and one fp32 (O, LSE) partial per chunk and query

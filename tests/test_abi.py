@@ -234,3 +234,20 @@ def test_validate_tables_accepts_good_and_flags_bad():
     assert sa.validate_tables(segs, ind, ck, w.pool_tokens, cu_seqlens_q=cq2) == (5, 2)
     assert sa.validate_tables(segs, ind, ck, w.pool_tokens, cu_seqlens_q=cq2, causal=False)[0] == 0
 
+
+def test_decode_noalloc_rejects_bad_arguments_and_calls_beyond_its_scratch():
+    """The no-allocation decode takes seg_attn_decode's arguments minus the workspace and checks
+    them the same way; a call whose plan needs more than its fixed 64 MiB scratch is refused with
+    SEG_ATTN_ERR_SCRATCH before anything is launched."""
+    lib = _lib()
+    a = _decode_args()
+    del a[19:21]  # no workspace, no workspace size
+    ok = list(a)
+    assert lib.seg_attn_decode_noalloc(*[None if i == 0 else x for i, x in enumerate(ok)]) == 1  # q NULL
+    bad = list(ok); bad[13] = 96  # head_dim
+    assert lib.seg_attn_decode_noalloc(*bad) == 2
+    bad = list(ok); bad[0] = 264  # misaligned q
+    assert lib.seg_attn_decode_noalloc(*bad) == 1
+    big = list(ok); big[10] = 64 * 100_000; big[16] = 100_000  # max_seqlen_k, num_splits
+    assert lib.seg_attn_decode_noalloc(*big) == 7
+    assert "scratch" in sa.status_string(7)
