@@ -389,11 +389,12 @@ def cpu_baseline(w, c: int):
             "sample": f"{what}, float64 numpy, best of {passes} pass(es): {best:.2f} s"}
 
 
-def measure(w, steps, warmup, kind, graph=False, loop_1000=False):
+def measure(w, steps, warmup, kind, graph=False, loop_1000=False, per_call=True):
     step = make_step(w)
     t = time_steps(step, steps, warmup, graph)
-    t.update(per_call_times(step))
-    if loop_1000:
+    if per_call:
+        t.update(per_call_times(step))
+    if loop_1000 and per_call:
         t["back_to_back_1000_us"] = back_to_back(step, 1000)
     if kind == "prefill":
         work = prefill_flops(w)
@@ -419,6 +420,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", type=int, default=2, help="headline workload (1..6)")
+    ap.add_argument("--no-per-call", action="store_true",
+                    help="only the K-step loop: no per-call events and no 1000-call loop (profiler runs)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph capturing one step instead of eager calls")
     ap.add_argument("--append-only", default=None, metavar="NAME|all",
@@ -488,7 +491,7 @@ def main():
     kind = w.kind
     log(f"[bench] timing {w.name}: warmup {args.warmup}, steps {args.steps}")
     value, unit, roof, t, work = measure(w, args.steps, args.warmup, kind, args.graph,
-                                         loop_1000=head_c in (1, 2))
+                                         loop_1000=head_c in (1, 2), per_call=not args.no_per_call)
     log(f"[bench] {w.name}: {value:.2f} {unit} per step, launch mean {t['launch_ms_mean']*1e3:.1f} us, "
         f"roofline frac {roof['frac']:.3f}")
 
@@ -522,9 +525,9 @@ def main():
             log(f"[bench] config {c}: generating")
             wc = wl.make_config(c, device=dev)
             v, u, rf, tc, wk = measure(wc, max(20, args.steps // 2), args.warmup, wc.kind, args.graph,
-                                       loop_1000=c in (1, 2))
+                                       loop_1000=c in (1, 2), per_call=not args.no_per_call)
             log(f"[bench] {wc.name}: {v:.2f} {u}, launch mean {tc['launch_ms_mean']*1e3:.1f} us, "
-                f"per-call median {tc['per_call_us_median']:.1f} us, frac {rf['frac']:.3f}")
+                f"per-call median {tc.get('per_call_us_median', float('nan')):.1f} us, frac {rf['frac']:.3f}")
             entry = {"workload": wc.name, "value": round(v, 3), "unit": u,
                      "launch_us_mean": round(tc["launch_ms_mean"] * 1e3, 2),
                      "timing": {k: round(x, 6) for k, x in tc.items()},
