@@ -41,14 +41,13 @@ constexpr float kRescaleLog2 = 8.0f;
 
 // LDS layouts (row = key within the block, 256 B = 16 chunks of 16 B per row):
 //   K: chunk c of row r is stored at chunk position c ^ (r % 16)
-//   V (128-row tiles): quarter-major, d quarter q (64 B of every row) of the block's 64 rows
-//     occupies bytes q * 4096 + r * 64 .. + 63
-//   V (256-row tiles): chunk c of row r is stored at chunk position c ^ vswz(r)
+//   V: quarter-major, d quarter q (64 B of every row) of the block's 64 rows occupies bytes
+//     q * 4096 + r * 64 .. + 63
+// (both tilings use these layouts).
 // K is read 16 B per lane over 32 consecutive rows, V with the transposing read over groups of
 // 4 consecutive rows. The K swizzle keeps its reads free of bank conflicts; in the quarter-major
 // V layout one transposing read covers 8 consecutive rows of one quarter, 512 contiguous bytes,
 // and every read of a block is a constant offset from a single per-lane address.
-__device__ __forceinline__ int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 __device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -106,8 +105,10 @@ __device__ __forceinline__ void mark_uncovered_rows(bf16_t* out, float* lse, int
 // 0-15 of the tile, group 1 positions 16-31; both groups consume every K/V block (so each block
 // copied into LDS serves 256 rows, half the L2->LDS traffic of the 128-row tiles) and run in
 // opposite phases: in step j group 0 issues its MFMAs (PV of block j-1, S of block j) while
-// group 1 runs the softmax of block j-1, then the roles swap. K and V blocks are double
-// buffered and copied one step ahead of use; the Q tile is staged in LDS.
+// group 1 runs the softmax of block j-1, then the roles swap. K and V blocks are copied from
+// HBM straight into LDS (double buffered): at the start of step j the copies of K(j+1) and V(j)
+// are issued into the slots freed by step j-1, and the step's last barrier waits for them. Each
+// wave's Q rows stay in registers.
 constexpr int kWidePos = 32;
 
 template <bool kCausal>
@@ -118,12 +119,17 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     const int32_t* __restrict__ cu_k, int batch, int hkv, int n_qtiles, float scale,
     float scale_log2, bf16_t* __restrict__ out, float* __restrict__ lse) {
   // Separate LDS objects per ring slot, indexed only by compile-time constants, so the compiler
-  // can tell the slots being read from the slots being filled.
-  __shared__ __attribute__((aligned(1024))) char kr0[kBlkBytes];
-  __shared__ __attribute__((aligned(1024))) char kr1[kBlkBytes];
-  __shared__ __attribute__((aligned(1024))) char vr0[kBlkBytes];
-  __shared__ __attribute__((aligned(1024))) char vr1[kBlkBytes];
-  __shared__ __attribute__((aligned(1024))) char qlds[2 * kWidePos * kGroup * kHeadDim];  // 256 rows
+  // can tell the slots being read from the slots being filled. The K and V slots get the larger
+  // alignments, which places them below 64 KiB: every K and V read is then a per-lane register
+  // plus an immediate offset.
+  __shared__ __attribute__((aligned(4096))) char vr0[kBlkBytes];
+  __shared__ __attribute__((aligned(4096))) char vr1[kBlkBytes];
+  __shared__ __attribute__((aligned(2048))) char kr0[kBlkBytes];
+  __shared__ __attribute__((aligned(2048))) char kr1[kBlkBytes];
+
+  // Every pointer argument in scalar registers before the first table read (one round trip).
+  asm volatile("" ::"s"(q), "s"(k_pool), "s"(v_pool), "s"(segs), "s"(seg_indptr), "s"(cu_q),
+               "s"(cu_k), "s"(out), "s"(lse));
 
   // Work item: kv head fastest (with 8 kv heads, head g always runs on XCD g), then the query
   // tiles of one request, heaviest (last) first, then the requests. Workgroups running at the
@@ -134,11 +140,19 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
   const int b = t / n_qtiles;
   const int qtile = n_qtiles - 1 - t % n_qtiles;
 
-  const int q0 = cu_q[b];
-  const int lq = cu_q[b + 1] - q0;
+  // The request's six table entries in one vector load (lanes 0-5), then broadcast.
+  int tv = 0;
+  {
+    const int tl = threadIdx.x & 63;
+    if (tl < 6) tv = (tl < 2 ? cu_q : (tl < 4 ? cu_k : seg_indptr))[b + (tl & 1)];
+  }
+  const int q0 = __builtin_amdgcn_readlane(tv, 0);
+  const int lq = __builtin_amdgcn_readlane(tv, 1) - q0;
+  const int K = __builtin_amdgcn_readlane(tv, 3) - __builtin_amdgcn_readlane(tv, 2);
+  const int seg_first = __builtin_amdgcn_readlane(tv, 4);
+  const int seg_last = __builtin_amdgcn_readlane(tv, 5);
   const int p0 = qtile * kWidePos;
   if (p0 >= lq) return;
-  const int K = cu_k[b + 1] - cu_k[b];
   const int hq = hkv * kGroup;
   if (qtile == n_qtiles - 1 && lq > n_qtiles * kWidePos)
     mark_uncovered_rows(out, lse, q0, n_qtiles * kWidePos, lq, hq, g);
@@ -161,85 +175,83 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
   const int kfull = kCausal ? min(K, K - lq + wpos0 + 1) : K;  // every row of this wave sees these
   const int row_limit = kCausal ? min(K, K - lq + pos + 1) : K;
 
-  // Q tile staged in LDS (kept out of registers): LDS row R = wave * 32 + n holds the query row
-  // of wave R / 32, lane row n; chunk c of row R sits at chunk position c ^ (R % 16). Thread t
-  // copies chunk position t % 16 of rows t / 16 + 32 i; rows past the request re-read its last
-  // query row (they are computed but never stored).
+  // Q fragments in registers: B operand of S^T = K Q^T. Lane holds d = 16 step + 8 h + (0..7)
+  // of its row; rows past the request are zero (computed, never stored).
+  bf16x8 qf[8];
   {
+    const bf16_t* qrow = q + ((int64_t)(q0 + pos) * hq + head) * kHeadDim + 8 * h;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int R = (tid >> 4) + 32 * i;
-      const int rw = R >> 5, rn = R & 31;
-      const int rpos = min(p0 + 16 * (rw >> 2) + 4 * (rw & 3) + (rn >> 3), lq - 1);
-      const int rhead = g * kGroup + (rn & 7);
-      const int c = (tid & 15) ^ (R & 15);
-      const bf16_t* src = q + ((int64_t)(q0 + rpos) * hq + rhead) * kHeadDim + c * 8;
-      copy16_to_lds(src, (lds_void_t*)((lds_char_t*)qlds + i * 8192 + wave * 1024));
-    }
+    for (int step = 0; step < 8; ++step)
+      qf[step] = row_valid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * step) : bf16x8{};
   }
-  const lds_char_t* qmine = (const lds_char_t*)qlds + (wave * 32 + n) * 256;
 
+  // ---- HBM -> LDS copies, 16 instructions of 1 KiB per block and tensor, two per wave.
+  // K instruction c = 2 w + i fills rows 4c .. 4c + 3 (lane L: row 4c + L / 16, the global chunk
+  // (L % 16) ^ (row % 16), so that chunk c of row r lands at chunk position c ^ (r % 16)).
+  // V instruction i of wave w fills d quarter w % 4 of rows 16 j .. 16 j + 15, j = 2 (w / 4) + i
+  // (lane L: row 16 j + L / 4, 16 bytes at quarter column L % 4): quarter-major.
   BlockCursor kcur, vcur;
-  kcur.init(segs, seg_indptr[b], seg_indptr[b + 1]);
-  vcur.init(segs, seg_indptr[b], seg_indptr[b + 1]);
-  const int crow = tid >> 4;
-  const int kchunk = (tid & 15) ^ (crow & 15);
-  const int vchunk = (tid & 15) ^ vswz(crow);
+  kcur.init(segs, seg_first, seg_last);
+  vcur.init(segs, seg_first, seg_last);
   const int64_t tok_stride = (int64_t)hkv * kHeadDim;
+  const uint32_t tok_bytes = (uint32_t)hkv * kHeadDim * 2;
   const bf16_t* kbase = k_pool + (int64_t)g * kHeadDim;
   const bf16_t* vbase = v_pool + (int64_t)g * kHeadDim;
-  const uint32_t tok_bytes = (uint32_t)hkv * kHeadDim * 2;
-  const uint32_t koff0 = (uint32_t)crow * tok_bytes + kchunk * 16, koff1 = koff0 + 32 * tok_bytes;
-  const uint32_t voff0 = (uint32_t)crow * tok_bytes + vchunk * 16, voff1 = voff0 + 32 * tok_bytes;
-
-  struct BlockAddr {
-    bool fast;
-    int64_t base, s0, s1;
-  };
-  auto block_addr = [&](BlockCursor& cur, int blk) __attribute__((always_inline)) {
-    BlockAddr a;
+  const int krow0 = 8 * wave + (lane >> 4);  // K row of instruction i: krow0 + 4 i
+  const int kch = lane & 15;
+  const int vrow0 = 32 * (wave >> 2) + (lane >> 2);  // V row of instruction i: vrow0 + 16 i
+  const uint32_t vcol = (uint32_t)(wave & 3) * 64 + (lane & 3) * 16;
+  const uint32_t vdst0 = (uint32_t)(wave & 3) * 4096 + (uint32_t)(wave >> 2) * 2048;
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    koff[i] = (uint32_t)(krow0 + 4 * i) * tok_bytes + ((kch ^ ((krow0 + 4 * i) & 15)) << 4);
+    voff[i] = (uint32_t)(vrow0 + 16 * i) * tok_bytes + vcol;
+  }
+  // Fast case (the block inside one segment and inside the request's keys): row r of the block
+  // is pool slot base + r, a scalar base plus a fixed per-thread offset. Otherwise every row is
+  // looked up on its own (rows past K re-read key K - 1, masked later).
+  auto issue_k = [&](int blk, char* dst) __attribute__((always_inline)) {
     const int kb0 = blk * kBlockN;
     const int last = min(kb0 + kBlockN, K) - 1;
-    cur.advance_to(kb0);
-    a.fast = (kb0 + kBlockN <= K) && (last - cur.start < cur.len);
-    a.base = (int64_t)cur.off + (kb0 - cur.start);
-    a.s0 = a.s1 = 0;
-    if (!a.fast) {
-      // Walk the segments the block overlaps with a scalar copy of the cursor: every lane
-      // takes the same trip and the table is read with scalar loads, so no vector memory
-      // wait (which would also wait for the prefetched K/V) is needed.
-      const int r0 = min(kb0 + crow, last), r1 = min(kb0 + 32 + crow, last);
-      BlockCursor c2 = cur;
-      while (true) {
-        if (r0 - c2.start >= 0 && r0 - c2.start < c2.len) a.s0 = (int64_t)c2.off + (r0 - c2.start);
-        if (r1 - c2.start >= 0 && r1 - c2.start < c2.len) a.s1 = (int64_t)c2.off + (r1 - c2.start);
-        if (last - c2.start < c2.len) break;
-        c2.start += c2.len;
-        ++c2.idx;
-        c2.fetch();
+    kcur.advance_to(kb0);
+    lds_char_t* l = (lds_char_t*)dst + wave * 2048;
+    if ((kb0 + kBlockN <= K) && (last - kcur.start < kcur.len)) {
+      const char* base = (const char*)(kbase + ((int64_t)kcur.off + (kb0 - kcur.start)) * tok_stride);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) copy16_to_lds(base + koff[i], (lds_void_t*)(l + 1024 * i));
+    } else {
+      SegCursor c2;
+      c2.segs = kcur.segs; c2.idx = kcur.idx; c2.end = kcur.end;
+      c2.start = kcur.start; c2.off = kcur.off; c2.len = kcur.len;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = krow0 + 4 * i;
+        const int64_t slot = c2.slot(min(kb0 + r, last));
+        copy16_to_lds((const char*)(kbase + slot * tok_stride) + ((kch ^ (r & 15)) << 4),
+                      (lds_void_t*)(l + 1024 * i));
       }
     }
-    return a;
   };
-  // K/V blocks travel HBM -> registers -> LDS. Loading into registers two steps ahead of the
-  // LDS write hides the HBM latency of blocks no workgroup has touched yet, and plain register
-  // loads let the compiler wait for exactly the data it needs.
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  auto load_rows = [&](BlockCursor& cur, int blk, const bf16_t* pool_base, int chunk, uint32_t off0,
-                       uint32_t off1, u32x4& r0, u32x4& r1) __attribute__((always_inline)) {
-    const BlockAddr a = block_addr(cur, blk);
-    // one load per row on every path (no branch around the loads), from either address form
-    const char* sb = (const char*)(pool_base + a.base * tok_stride);
-    const char* p0 = a.fast ? sb + off0 : (const char*)(pool_base + a.s0 * tok_stride + chunk * 8);
-    const char* p1 = a.fast ? sb + off1 : (const char*)(pool_base + a.s1 * tok_stride + chunk * 8);
-    r0 = *(const u32x4*)p0;
-    r1 = *(const u32x4*)p1;
-  };
-  // Thread tid's two 16-byte pieces of a block go to bytes tid*16 and 8192 + tid*16 of its slot
-  // (the swizzle is in which global chunk the thread loaded).
-  auto store_rows = [&](char* dst, const u32x4& r0, const u32x4& r1) __attribute__((always_inline)) {
-    *(__attribute__((address_space(3))) u32x4*)((lds_char_t*)dst + tid * 16) = r0;
-    *(__attribute__((address_space(3))) u32x4*)((lds_char_t*)dst + 8192 + tid * 16) = r1;
+  auto issue_v = [&](int blk, char* dst) __attribute__((always_inline)) {
+    const int kb0 = blk * kBlockN;
+    const int last = min(kb0 + kBlockN, K) - 1;
+    vcur.advance_to(kb0);
+    lds_char_t* l = (lds_char_t*)dst + vdst0;
+    if ((kb0 + kBlockN <= K) && (last - vcur.start < vcur.len)) {
+      const char* base = (const char*)(vbase + ((int64_t)vcur.off + (kb0 - vcur.start)) * tok_stride);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) copy16_to_lds(base + voff[i], (lds_void_t*)(l + 1024 * i));
+    } else {
+      SegCursor c2;
+      c2.segs = vcur.segs; c2.idx = vcur.idx; c2.end = vcur.end;
+      c2.start = vcur.start; c2.off = vcur.off; c2.len = vcur.len;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t slot = c2.slot(min(kb0 + vrow0 + 16 * i, last));
+        copy16_to_lds((const char*)(vbase + slot * tok_stride) + vcol, (lds_void_t*)(l + 1024 * i));
+      }
+    }
   };
 
   f32x16 o[4];
@@ -253,42 +265,61 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
   float l_run = 0.f;
   const int G = lane >> 4;
   const int sl = lane & 15;
+  // V^T operands (quarter-major V): lane reads rows 16 u + 4 h + sl / 4 (and + 8) at d offset
+  // 16 (G % 2) + 4 (sl % 4) of quarter dt; every read is this per-lane offset plus a constant.
+  const uint32_t vlane = (uint32_t)(4 * h + (sl >> 2)) * 64 + 32 * (G & 1) + 8 * (sl & 3);
+  // K operands: chunk 2 step + h of row n sits at chunk position (2 step + h) ^ (n % 16).
+  uint32_t kofs[8];
+#pragma unroll
+  for (int step = 0; step < 8; ++step) kofs[step] = (uint32_t)(n * 256 + (((2 * step + h) ^ (n & 15)) << 4));
 
+  // MFMA phase of step j: O^T += V^T P^T for block j - 1, then S^T = K Q^T for block j. LDS
+  // operands are read ahead of the MFMAs that use them (V one d tile ahead, K two k-steps
+  // ahead).
   auto gemm_phase = [&](int j, const char* vprev, const char* kcurp) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     if (j >= 1) {
-      const lds_char_t* vb = (const lds_char_t*)vprev;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int dcol = 32 * dt + 16 * (G & 1) + 4 * (sl & 3);
-        const int chunk = dcol >> 3;
-        const int within = (dcol & 7) * 2;
+      const lds_char_t* vb = (const lds_char_t*)vprev + vlane;
+      auto read_vt = [&](int dt, bf16x8 (&dst)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int ra = 16 * u + 4 * h + (sl >> 2);
-          const int rb = ra + 8;
-          bf16x4 lo = lds_read_tr16(vb + ra * 256 + ((chunk ^ vswz(ra)) << 4) + within);
-          bf16x4 hi = lds_read_tr16(vb + rb * 256 + ((chunk ^ vswz(rb)) << 4) + within);
-          bf16x8 a;
-          a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-          a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-          o[dt] = mfma32x32x16(a, pb[u], o[dt]);
+          bf16x4 lo = lds_read_tr16(vb + (dt * 4096 + u * 1024));
+          bf16x4 hi = lds_read_tr16(vb + (dt * 4096 + u * 1024 + 512));
+          dst[u][0] = lo[0]; dst[u][1] = lo[1]; dst[u][2] = lo[2]; dst[u][3] = lo[3];
+          dst[u][4] = hi[0]; dst[u][5] = hi[1]; dst[u][6] = hi[2]; dst[u][7] = hi[3];
         }
+      };
+      bf16x8 va[2][4];
+      read_vt(0, va[0]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        if (dt + 1 < 4) read_vt(dt + 1, va[(dt + 1) & 1]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[dt] = mfma32x32x16(va[dt & 1][u], pb[u], o[dt]);
+        if (dt + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (j < n_blocks) {
       const lds_char_t* kb = (const lds_char_t*)kcurp;
-      s0 = f32x16{};
-      s1 = f32x16{};
+      bf16x8 ka[3][2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        ka[st][0] = lds_read16(kb + kofs[st]);
+        ka[st][1] = lds_read16(kb + kofs[st] + 32 * 256);
+      }
 #pragma unroll
       for (int step = 0; step < 8; ++step) {
-        const int c = 2 * step + h;
-        const int r0 = n, r1 = 32 + n;
-        bf16x8 a0 = lds_read16(kb + r0 * 256 + ((c ^ (r0 & 15)) << 4));
-        bf16x8 a1 = lds_read16(kb + r1 * 256 + ((c ^ (r1 & 15)) << 4));
-        const bf16x8 qv = lds_read16(qmine + ((c ^ (n & 15)) << 4));
-        s0 = mfma32x32x16(a0, qv, s0);
-        s1 = mfma32x32x16(a1, qv, s1);
+        if (step + 2 < 8) {
+          ka[(step + 2) % 3][0] = lds_read16(kb + kofs[step + 2]);
+          ka[(step + 2) % 3][1] = lds_read16(kb + kofs[step + 2] + 32 * 256);
+        }
+        s0 = mfma32x32x16(ka[step % 3][0], qf[step], step == 0 ? f32x16{} : s0);
+        s1 = mfma32x32x16(ka[step % 3][1], qf[step], step == 0 ? f32x16{} : s1);
+        if (step + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -338,51 +369,38 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     pb[3] = to_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
   };
 
-  // Register staging sets: set e holds K(j+1) and V(j) at the start of step j with j % 2 == e.
-  u32x4 stk[2][2], stv[2][2];
-  const int last_blk = n_blocks - 1;
-
-  // Step j: K(j) in LDS slot j % 2 is read (S of block j), V(j-1) in slot (j-1) % 2 is read
-  // (PV of block j-1). At the start, staging set j % 2 (loaded two steps earlier) is written to
-  // LDS: K(j+1) into slot (j+1) % 2 and V(j) into slot j % 2, both last read in step j-1; then
-  // the same set is refilled with K(j+3) and V(j+2). Blocks past the end re-load the last one.
+  // Step j: K(j) in slot j % 2 is read (S of block j), V(j-1) in slot (j-1) % 2 (PV of block
+  // j-1). At its start the copies of K(j+1) into slot (j+1) % 2 and of V(j) into slot j % 2 are
+  // issued: both slots were last read in step j-1, which ended with a barrier. Its last barrier
+  // follows the wait for those copies. (A third slot, copying two steps ahead, measured no
+  // faster on the chunked prefill.)
   auto step = [&](int j, auto r_c) __attribute__((always_inline)) {
     constexpr int R = decltype(r_c)::value;
     char* kread = R == 0 ? kr0 : kr1;
     char* kwrite = R == 0 ? kr1 : kr0;
     char* vread = R == 0 ? vr1 : vr0;
     char* vwrite = R == 0 ? vr0 : vr1;
-    store_rows(kwrite, stk[R][0], stk[R][1]);
-    store_rows(vwrite, stv[R][0], stv[R][1]);
-    load_rows(kcur, min(j + 3, last_blk), kbase, kchunk, koff0, koff1, stk[R][0], stk[R][1]);
-    load_rows(vcur, min(j + 2, last_blk), vbase, vchunk, voff0, voff1, stv[R][0], stv[R][1]);
+    // Both cursors move first: a segment-table read waits for every vector memory operation
+    // in flight, so it must not come after this step's first copies.
+    if (j + 1 < n_blocks) kcur.advance_to((j + 1) * kBlockN);
+    if (j < n_blocks) vcur.advance_to(j * kBlockN);
+    if (j + 1 < n_blocks) issue_k(j + 1, kwrite);
+    if (j < n_blocks) issue_v(j, vwrite);
     if (grp == 0) gemm_phase(j, vread, kread);
     else softmax_phase(j - 1);
     phase_barrier();
     if (grp == 1) gemm_phase(j, vread, kread);
     else softmax_phase(j);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this step's LDS stores are done
+    wait_vmem();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     phase_barrier();
   };
 
-  // Prologue: K(0) into slot 0; staging set 0 = {K(1), V(0)}, set 1 = {K(2), V(1)}.
-  if (n_blocks > 0) {
-    u32x4 a0, a1;
-    // issue order = use order (set 0 before set 1), so each wait covers only what it needs
-    load_rows(kcur, 0, kbase, kchunk, koff0, koff1, a0, a1);
-    load_rows(kcur, min(1, last_blk), kbase, kchunk, koff0, koff1, stk[0][0], stk[0][1]);
-    load_rows(vcur, 0, vbase, vchunk, voff0, voff1, stv[0][0], stv[0][1]);
-    load_rows(kcur, min(2, last_blk), kbase, kchunk, koff0, koff1, stk[1][0], stk[1][1]);
-    load_rows(vcur, min(1, last_blk), vbase, vchunk, voff0, voff1, stv[1][0], stv[1][1]);
-    store_rows(kr0, a0, a1);
-  }
-  wait_vmem();  // also the Q tile's HBM->LDS copies
-  __builtin_amdgcn_s_waitcnt(0xC07F);
+  if (n_blocks > 0) issue_k(0, kr0);
+  wait_vmem();  // also the Q loads
   phase_barrier();
   if (n_blocks > 0) {
-    // Both steps of a pair unconditionally inside the loop, the odd tail after it: a loop body
-    // that may end after its first step would make the compiler assume that step's loads are
-    // the most recent ones at the loop head and wait for all of them.
+    // Both steps of a pair unconditionally inside the loop, the odd tail after it.
     int j = 0;
     for (; j + 1 <= n_blocks; j += 2) {
       step(j, std::integral_constant<int, 0>{});
