@@ -22,7 +22,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "decode", "decode_noalloc", "kv_append", "linear_prefill", "linear_decode", "SegmentAllocator",
+__all__ = ["prefill", "decode", "decode_noalloc", "kv_append", "kv_move", "linear_prefill", "linear_decode", "SegmentAllocator",
            "decode_num_splits", "decode_workspace_bytes", "validate_tables",
            "status_string", "version", "library_path", "SegAttnError", "KV_BF16", "KV_FP8_E4M3",
            "KV_INT8"]
@@ -109,6 +109,10 @@ def _load():
     lib.seg_attn_allocator_stats.restype = I32
     lib.seg_attn_allocator_free_runs.argtypes = [P, P, I64, PI64]
     lib.seg_attn_allocator_free_runs.restype = I32
+    lib.seg_attn_allocator_compact.argtypes = [P, P, I64, PI64]
+    lib.seg_attn_allocator_compact.restype = I32
+    lib.seg_attn_kv_move.argtypes = [P, I32, I64, I32, I32, I64, I32, P, P, P, P, P]
+    lib.seg_attn_kv_move.restype = I32
     _lib = lib
     return lib
 
@@ -387,6 +391,47 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, segs: torch.Tensor, seg_
         raise SegAttnError("seg_attn_kv_append", st)
 
 
+def kv_move(moves: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, *,
+            k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+            total_tokens: Optional[int] = None) -> None:
+    """Apply a compaction's moves to the pools in place (seg_attn_kv_move). moves: int32 [n, 4]
+    (src_offset, dst_offset, length, first) on the pools' device; total_tokens (the sum of the
+    lengths) is read from the tensor unless given."""
+    lib = _load()
+    dev = k_pool.device
+    if dev.type != "cuda":
+        raise ValueError("k_pool must be a GPU tensor")
+    if k_pool.dtype not in _KV_OF_DTYPE:
+        raise TypeError(f"k_pool has dtype {k_pool.dtype}: expected bfloat16, float8_e4m3fn or int8")
+    kv_dtype = _KV_OF_DTYPE[k_pool.dtype]
+    scaled = kv_dtype != KV_BF16
+    _check(k_pool, "k_pool", (k_pool.dtype,), dev, 3)
+    _check(v_pool, "v_pool", (k_pool.dtype,), dev, 3)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape")
+    _check(moves, "moves", (torch.int32,), dev, 2)
+    if moves.shape[1] != 4:
+        raise ValueError("moves must have shape [n, 4]")
+    pool_tokens, hkv, d = k_pool.shape
+    if scaled:
+        if k_scale is None or v_scale is None:
+            raise ValueError("an fp8 or int8 pool needs k_scale and v_scale")
+        for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            _check(t, nm, (torch.float32,), dev, 2)
+            if tuple(t.shape) != (pool_tokens, hkv):
+                raise ValueError(f"{nm} must have shape [pool_tokens, Hkv]")
+    n = moves.shape[0]
+    if total_tokens is None:
+        total_tokens = int(moves[:, 2].sum().item()) if n else 0
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.seg_attn_kv_move(_ptr(moves), n, int(total_tokens), hkv, d, pool_tokens, kv_dtype,
+                                  _ptr(k_pool), _ptr(v_pool), _ptr(k_scale if scaled else None),
+                                  _ptr(v_scale if scaled else None), stream)
+    if st != 0:
+        raise SegAttnError("seg_attn_kv_move", st)
+
+
 def _check_linear(q, k, v, g, state_slots, state_pool, batch):
     dev = q.device
     if dev.type != "cuda":
@@ -573,6 +618,24 @@ class SegmentAllocator:
         runs = np.zeros((max(int(cnt.value), 1), 2), dtype=np.int32)
         self._call("seg_attn_allocator_free_runs", runs.ctypes.data, runs.shape[0], ctypes.byref(cnt))
         return runs[:int(cnt.value)]
+
+    def compact(self):
+        """Relocate fragmented requests into single ranges (seg_attn_allocator_compact). Returns
+        the moves as a host int32 array [n, 4] of (src_offset, dst_offset, length, first); apply
+        them to the pools with kv_move before using new tables."""
+        import numpy as np
+        if self._h is None:
+            raise RuntimeError("allocator is closed")
+        cnt = ctypes.c_int64(0)
+        moves = np.zeros((64, 4), dtype=np.int32)
+        while True:
+            st = self._lib.seg_attn_allocator_compact(self._h, moves.ctypes.data, moves.shape[0],
+                                                      ctypes.byref(cnt))
+            if st == 0:
+                return moves[:int(cnt.value)]
+            if st != 3:
+                raise SegAttnError("seg_attn_allocator_compact", st)
+            moves = np.zeros((int(cnt.value), 4), dtype=np.int32)
 
     def tables(self, requests):
         import numpy as np

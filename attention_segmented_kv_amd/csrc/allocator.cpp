@@ -15,11 +15,18 @@
 // nothing. Release and truncate free slots (truncate also the spare capacity), merging them with
 // neighbouring free runs.
 //
+// Compaction relocates fragmented requests (two or more ranges), most ranges first, then by
+// increasing id, each whole into the smallest free run of the call's start (lowest start among
+// equals) that holds its capacity; slots it frees are not reused in the same call, so every
+// destination is disjoint from every source and every other destination and the caller may apply
+// the moves in any order or all at once (seg_attn_kv_move).
+//
 // Free runs are kept twice: by start (to find a neighbour and the run after a segment) and by
 // (length, start) (best fit and largest run), so every step is logarithmic in the number of
 // runs. Requests map to their segment lists.
 #include <stdint.h>
 
+#include <algorithm>
 #include <iterator>
 #include <map>
 #include <new>
@@ -58,6 +65,16 @@ struct seg_attn_allocator {
     const int64_t start = it->first, len = it->second;
     drop_run(it);
     if (len > n) add_run(start + n, len - n);
+    free_tokens -= n;
+  }
+
+  // Take [start, start + n) out of the free run that holds it.
+  void take_range(int64_t start, int64_t n) {
+    auto it = std::prev(by_start.upper_bound(start));
+    const int64_t rs = it->first, rl = it->second;
+    drop_run(it);
+    if (start > rs) add_run(rs, start - rs);
+    if (start + n < rs + rl) add_run(start + n, rs + rl - (start + n));
     free_tokens -= n;
   }
 
@@ -225,6 +242,62 @@ seg_attn_status_t seg_attn_allocator_truncate(seg_attn_allocator_t* a, int64_t r
       req.capacity -= cut;
     }
     req.keys = new_length;
+    return SEG_ATTN_OK;
+  } catch (...) {
+    return SEG_ATTN_ERR_OUT_OF_MEMORY;
+  }
+}
+
+seg_attn_status_t seg_attn_allocator_compact(seg_attn_allocator_t* a, seg_attn_move_t* moves,
+                                             int64_t capacity, int64_t* n_moves) {
+  if (n_moves) *n_moves = 0;
+  if (a == nullptr || capacity < 0) return SEG_ATTN_ERR_INVALID_ARG;
+  try {
+    // Plan on a snapshot of the free runs (by (length, start) for best fit); nothing changes
+    // unless the moves fit in the caller's array.
+    std::set<std::pair<int64_t, int64_t>> runs;
+    for (const auto& r : a->by_start) runs.emplace(r.second, r.first);
+    std::vector<std::pair<int64_t, int64_t>> order;  // (-number of ranges, id)
+    for (const auto& kv : a->requests)
+      if (kv.second.ranges.size() >= 2) order.emplace_back(-(int64_t)kv.second.ranges.size(), kv.first);
+    std::sort(order.begin(), order.end());
+    std::vector<std::pair<int64_t, int64_t>> plan;  // (id, destination start)
+    int64_t count = 0;
+    for (const auto& o : order) {
+      const Request& req = a->requests.at(o.second);
+      auto fit = runs.lower_bound({req.capacity, INT64_MIN});
+      if (fit == runs.end()) continue;
+      const int64_t start = fit->second, len = fit->first;
+      runs.erase(fit);
+      if (len > req.capacity) runs.emplace(len - req.capacity, start + req.capacity);
+      plan.emplace_back(o.second, start);
+      int64_t left = req.keys;
+      for (const seg_attn_segment_t& sg : req.ranges) {
+        if (left <= 0) break;
+        ++count;
+        left -= sg.length;
+      }
+    }
+    if (n_moves) *n_moves = count;
+    if (count > capacity || (count > 0 && moves == nullptr)) return SEG_ATTN_ERR_WORKSPACE;
+    int64_t m = 0, first = 0;
+    for (const auto& pl : plan) {
+      Request& req = a->requests.at(pl.first);
+      const int64_t dst = pl.second;
+      a->take_range(dst, req.capacity);
+      int64_t left = req.keys, done = 0;
+      for (const seg_attn_segment_t& sg : req.ranges) {
+        const int64_t n = left < sg.length ? left : sg.length;
+        if (n > 0) {
+          moves[m++] = {sg.pool_offset, (int32_t)(dst + done), (int32_t)n, (int32_t)first};
+          first += n;
+        }
+        done += n;
+        left -= n;
+      }
+      for (const seg_attn_segment_t& sg : req.ranges) a->give_back(sg.pool_offset, sg.length);
+      req.ranges.assign(1, seg_attn_segment_t{(int32_t)dst, (int32_t)req.capacity});
+    }
     return SEG_ATTN_OK;
   } catch (...) {
     return SEG_ATTN_ERR_OUT_OF_MEMORY;

@@ -26,6 +26,9 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const void* se
                             int batch, int total_new, int hkv, int64_t pool_tokens, int fmt,
                             void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                             hipStream_t stream);
+hipError_t launch_kv_move(const void* moves, int n_moves, int64_t total_tokens, int hkv,
+                          int64_t pool_tokens, int fmt, void* k_pool, void* v_pool, float* k_scale,
+                          float* v_scale, hipStream_t stream);
 hipError_t launch_linear_prefill(const void* q, const void* k, const void* v, const float* g,
                                  const int32_t* cu, const int32_t* slots, int batch, int heads,
                                  float scale, int initial_state, float* pool, int64_t pool_slots,
@@ -373,6 +376,33 @@ seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
                                              cu_seqlens_k, batch, total_new, num_heads_kv,
                                              pool_tokens, kv_dtype, k_pool, v_pool, k_scale,
                                              v_scale, (hipStream_t)stream);
+    return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
+  } catch (...) {
+    return SEG_ATTN_ERR_HIP;
+  }
+}
+
+seg_attn_status_t seg_attn_kv_move(const seg_attn_move_t* moves, int32_t n_moves,
+                                   int64_t total_tokens, int32_t num_heads_kv, int32_t head_dim,
+                                   int64_t pool_tokens, int32_t kv_dtype, void* k_pool,
+                                   void* v_pool, float* k_scale, float* v_scale,
+                                   seg_attn_stream_t stream) {
+  try {
+    if (n_moves < 0 || total_tokens < 0 || num_heads_kv <= 0 || head_dim <= 0 || pool_tokens < 0)
+      return SEG_ATTN_ERR_INVALID_ARG;
+    if (!valid_kv_dtype(kv_dtype)) return SEG_ATTN_ERR_INVALID_ARG;
+    if (head_dim != kHeadDim) return SEG_ATTN_ERR_UNSUPPORTED;
+    if (pool_tokens > INT32_MAX || total_tokens > pool_tokens) return SEG_ATTN_ERR_INVALID_ARG;
+    if (n_moves == 0 || total_tokens == 0) return SEG_ATTN_OK;
+    const bool scaled = kv_dtype != SEG_ATTN_KV_BF16;
+    if (!moves || !k_pool || !v_pool || (scaled && (!k_scale || !v_scale))) return SEG_ATTN_ERR_INVALID_ARG;
+    if (misaligned(moves, 16) || misaligned(k_pool, scaled ? 8 : 16) || misaligned(v_pool, scaled ? 8 : 16) ||
+        (scaled && (misaligned(k_scale, 4) || misaligned(v_scale, 4))))
+      return SEG_ATTN_ERR_INVALID_ARG;
+    if (total_tokens * num_heads_kv / 16 + 1 > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
+    hipError_t e = segattn::launch_kv_move(moves, n_moves, total_tokens, num_heads_kv, pool_tokens,
+                                           kv_dtype, k_pool, v_pool, k_scale, v_scale,
+                                           (hipStream_t)stream);
     return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;
   } catch (...) {
     return SEG_ATTN_ERR_HIP;

@@ -291,7 +291,72 @@ __global__ __launch_bounds__(256) void kv_append_token_kernel(
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// KV move: the pool side of the allocator's compaction. A move copies the rows of `len`
+// consecutive pool slots (every kv head; K, V and, for one-byte pools, their scales) from
+// slot src to slot dst. Moves are listed with `first`, the number of slots of all earlier moves,
+// so flattened slot t of the list belongs to the last move whose first <= t. The allocator only
+// plans moves whose sources and destinations are pairwise disjoint, so every row is copied
+// independently: one 16-lane group per (slot, kv head) row, 16 rows per workgroup.
+struct Move {
+  int32_t src, dst, len, first;
+};
+
+template <bool kOneByte>
+__global__ __launch_bounds__(256) void kv_move_kernel(const Move* __restrict__ moves, int n_moves,
+                                                      int64_t total_rows, int hkv, int64_t pool_tokens,
+                                                      char* __restrict__ k_pool, char* __restrict__ v_pool,
+                                                      float* __restrict__ k_scale,
+                                                      float* __restrict__ v_scale) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  if (row >= total_rows) return;
+  const int l16 = threadIdx.x & 15;
+  const int64_t t = row / hkv;
+  const int g = (int)(row - t * hkv);
+  // the last move with first <= t
+  int lo = 0, hi = n_moves - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (moves[mid].first <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const Move mv = moves[lo];
+  const int64_t k = t - mv.first;
+  if (k < 0 || k >= mv.len) return;  // a list whose `first` values do not add up
+  const int64_t src = (int64_t)mv.src + k, dst = (int64_t)mv.dst + k;
+  if (src < 0 || src >= pool_tokens || dst < 0 || dst >= pool_tokens) return;
+  constexpr int64_t kRowBytes = kOneByte ? 128 : 256;
+  const int64_t so = (src * hkv + g) * kRowBytes, dO = (dst * hkv + g) * kRowBytes;
+  if constexpr (kOneByte) {
+    const u32x2 kv = *reinterpret_cast<const u32x2*>(k_pool + so + 8 * l16);
+    const u32x2 vv = *reinterpret_cast<const u32x2*>(v_pool + so + 8 * l16);
+    *reinterpret_cast<u32x2*>(k_pool + dO + 8 * l16) = kv;
+    *reinterpret_cast<u32x2*>(v_pool + dO + 8 * l16) = vv;
+    if (l16 == 0) {
+      k_scale[dst * hkv + g] = k_scale[src * hkv + g];
+      v_scale[dst * hkv + g] = v_scale[src * hkv + g];
+    }
+  } else {
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(k_pool + so + 16 * l16);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(v_pool + so + 16 * l16);
+    *reinterpret_cast<u32x4*>(k_pool + dO + 16 * l16) = kv;
+    *reinterpret_cast<u32x4*>(v_pool + dO + 16 * l16) = vv;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_move(const void* moves, int n_moves, int64_t total_tokens, int hkv,
+                          int64_t pool_tokens, int fmt, void* k_pool, void* v_pool, float* k_scale,
+                          float* v_scale, hipStream_t stream) {
+  const int64_t rows = total_tokens * hkv;
+  const int64_t grid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (grid == 0 || n_moves == 0) return hipSuccess;
+  auto kern = fmt != 0 ? kv_move_kernel<true> : kv_move_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, (const Move*)moves, n_moves, rows,
+                     hkv, pool_tokens, (char*)k_pool, (char*)v_pool, k_scale, v_scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const void* segs,
                             const int32_t* seg_indptr, const int32_t* cu_new, const int32_t* cu_k,

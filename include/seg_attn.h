@@ -335,6 +335,51 @@ seg_attn_status_t seg_attn_allocator_tables(const seg_attn_allocator_t* allocato
                                             int32_t* seg_indptr, int32_t* cu_seqlens_k,
                                             int64_t* nseg);
 
+/*
+ * Compaction: relocate fragmented requests so that each becomes one contiguous range, the
+ * continuity the Flood README ("Introduction") keeps each request's cache in segmentable blocks
+ * for. Requests owning two or more ranges are taken in order of decreasing range count, then
+ * increasing id; each moves whole (its capacity C) into the smallest free run that existed when
+ * the call began and still holds C (lowest start among equals), from the run's start; a request
+ * that fits nowhere stays as it is. Slots the call frees are not reused within it, so every
+ * destination is disjoint from every source and from every other destination.
+ *
+ * The allocator's state (tables, free runs) is updated at once; the pool data must then be moved
+ * with seg_attn_kv_move (HOST moves copied to the device) before the new tables are used and
+ * before any further append. moves [capacity] receives one record per key-holding range of a
+ * relocated request: copy `length` slots from src_offset to dst_offset; `first` is the number of
+ * slots of all earlier records. *n_moves (if not NULL) receives the number of records; when it
+ * exceeds capacity nothing changes and SEG_ATTN_ERR_WORKSPACE is returned.
+ */
+typedef struct {
+  int32_t src_offset;
+  int32_t dst_offset;
+  int32_t length;
+  int32_t first;
+} seg_attn_move_t;
+seg_attn_status_t seg_attn_allocator_compact(seg_attn_allocator_t* allocator, seg_attn_move_t* moves,
+                                             int64_t capacity, int64_t* n_moves);
+
+/*
+ * KV move: apply a move list (from seg_attn_allocator_compact) to the pools on the device. For
+ * each record, the rows of slots src_offset .. src_offset + length - 1 (every kv head; K, V and,
+ * for FP8 / INT8 pools, their scales) are copied to the slots from dst_offset. The records'
+ * sources and destinations must be pairwise disjoint (the allocator plans them so); rows are
+ * copied in parallel, in no particular order.
+ * moves        [n_moves] seg_attn_move_t, DEVICE, 16-byte aligned; `first` must be the running
+ *              sum of the earlier records' lengths.
+ * total_tokens HOST, the sum of all lengths (it sizes the launch); at most pool_tokens.
+ * k_pool/v_pool/k_scale/v_scale as for seg_attn_kv_append (bf16 pools 16-byte aligned, one-byte
+ *              pools 8-byte, scales 4-byte; scales ignored for bf16).
+ * A slot outside [0, pool_tokens) is skipped, never accessed.
+ * Returns SEG_ATTN_OK, or an error before anything is launched.
+ */
+seg_attn_status_t seg_attn_kv_move(const seg_attn_move_t* moves, int32_t n_moves,
+                                   int64_t total_tokens, int32_t num_heads_kv, int32_t head_dim,
+                                   int64_t pool_tokens, int32_t kv_dtype, void* k_pool,
+                                   void* v_pool, float* k_scale, float* v_scale,
+                                   seg_attn_stream_t stream);
+
 /* Free slot count, longest free run, number of free runs and of live requests (any may be NULL). */
 seg_attn_status_t seg_attn_allocator_stats(const seg_attn_allocator_t* allocator,
                                            int64_t* free_tokens, int64_t* largest_free_run,

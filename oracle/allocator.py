@@ -25,6 +25,23 @@ implemented by the library) is the plainest one that serves that aim:
 - releasing a request frees all its slots; truncating it to L' < L keys frees every slot after
   its first L' (spare capacity included).
 
+Compaction (the pages name the aim, each request's cache kept contiguous, but no procedure; the
+reading modelled here) relocates fragmented requests into single ranges without ever moving data
+over data that is still to be moved:
+
+- the free runs at the start of the call are the only destinations (slots freed by the call itself
+  are not reused in it), so every destination lies in space that held no live data;
+- requests owning two or more ranges are taken in order of decreasing range count, then
+  increasing request id; each goes, whole (capacity C), into the smallest of those runs that holds
+  C (lowest start among equals), from the run's start, the rest of the run staying available; a
+  request that fits nowhere is left as it is;
+- a relocated request owns the one range [s, s + C) afterwards, its L keys being its first L
+  slots; its old ranges are freed; the moves copy each old range's key slots, in key order, to
+  consecutive slots from s.
+
+Every destination is then disjoint from every source and from every other destination, so the
+moves may be applied in any order, or all at once.
+
 The model keeps one boolean per pool slot and finds free runs by scanning it, so that it can be
 checked by eye; it is slow and meant for small pools.
 """
@@ -177,6 +194,35 @@ class AllocatorModel:
             excess -= cut
         self.keys[request] = new_length
 
+    def compact(self) -> List[Tuple[int, int, int]]:
+        """Relocate fragmented requests as described in the module docstring. Returns the moves
+        (src_offset, dst_offset, length) the pool data must undergo, in plan order."""
+        runs = [list(r) for r in self.free_runs()]  # destinations: the free space at the start
+        order = sorted((r for r, sg in self.segs.items() if len(sg) >= 2),
+                       key=lambda r: (-len(self.segs[r]), r))
+        moves = []
+        for r in order:
+            cap = self.capacity(r)
+            fits = [i for i, (st, ln) in enumerate(runs) if ln >= cap]
+            if not fits:
+                continue
+            i = min(fits, key=lambda i: (runs[i][1], runs[i][0]))
+            dst = runs[i][0]
+            runs[i][0] += cap
+            runs[i][1] -= cap
+            left, done = self.length(r), 0
+            for off, ln in self.segs[r]:
+                n = min(ln, left)
+                if n > 0:
+                    moves.append((off, dst + done, n))
+                done += n
+                left -= n
+            for off, ln in self.segs[r]:
+                self.used[off:off + ln] = False
+            self._take(dst, cap)
+            self.segs[r] = [[dst, cap]]
+        return moves
+
     # ---------------------------------------------------------------- tables
 
     def tables(self, requests: Sequence[int]):
@@ -190,3 +236,12 @@ class AllocatorModel:
             cu.append(cu[-1] + sum(ln for _, ln in s))
         segs = np.array(rows, dtype=np.int64).reshape(-1, 2)
         return segs, np.array(ind, dtype=np.int64), np.array(cu, dtype=np.int64)
+
+
+def apply_moves(pool: np.ndarray, moves: Sequence[Tuple[int, int, int]]) -> np.ndarray:
+    """A copy of `pool` (first axis = slots) with every move's source slots copied to its
+    destination slots, one move after the other."""
+    out = np.array(pool, copy=True)
+    for src, dst, n in moves:
+        out[dst:dst + n] = out[src:src + n]
+    return out

@@ -251,3 +251,21 @@ def test_decode_noalloc_rejects_bad_arguments_and_calls_beyond_its_scratch():
     big = list(ok); big[10] = 64 * 100_000; big[16] = 100_000  # max_seqlen_k, num_splits
     assert lib.seg_attn_decode_noalloc(*big) == 7
     assert "scratch" in sa.status_string(7)
+
+
+def _move_args(**over):
+    a = dict(moves=256, n=3, total=10, hkv=8, d=128, pool=100, kvd=0, kp=256, vp=256, ks=None, vs=None,
+             stream=None)
+    a.update(over)
+    return [a[k] for k in ("moves", "n", "total", "hkv", "d", "pool", "kvd", "kp", "vp", "ks", "vs", "stream")]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(moves=None), 1), (dict(n=-1), 1), (dict(total=-1), 1), (dict(hkv=0), 1), (dict(d=64), 2),
+    (dict(kvd=5), 1), (dict(kvd=1), 1), (dict(kp=None), 1), (dict(total=101), 1), (dict(moves=264), 1),
+    (dict(kp=264), 1), (dict(kvd=1, ks=4, vs=6, kp=8, vp=8), 1), (dict(pool=2 ** 31), 1),
+    (dict(n=0, moves=None), 0), (dict(total=0), 0),
+])
+def test_kv_move_rejects_bad_arguments(over, status):
+    lib = _lib()
+    assert lib.seg_attn_kv_move(*_move_args(**over)) == status

@@ -65,10 +65,19 @@ def test_matches_the_model_on_random_sequences(seed, pool, nreq, maxn, granule):
         elif op < 0.8:
             m.release(r)
             a.release(r)
-        else:
+        elif op < 0.97:
             keep = int(rng.integers(0, m.length(r) + 2))
             m.truncate(r, keep)
             a.truncate(r, keep)
+        else:
+            # compaction: the same moves (src, dst, length) in the same order, `first` their
+            # running sum
+            mm = m.compact()
+            am = a.compact()
+            assert am.shape == (len(mm), 4)
+            assert [tuple(x) for x in am[:, :3].tolist()] == mm
+            assert am[:, 3].tolist() == np.concatenate([[0], np.cumsum(am[:, 2])])[:-1].tolist()
+            _same_state(a, m, reqs)
         assert a.length(r) == m.length(r) and a.capacity(r) == m.capacity(r)
         if step % 10 == 0 or step > 780:
             _same_state(a, m, reqs)
@@ -178,3 +187,22 @@ def test_tables_feed_validate_tables():
     reqs = list(range(40))
     segs, ind, cu = a.tables(reqs)
     assert sa.validate_tables(segs, ind, cu, 5000, causal=False) == (0, -1)
+
+
+def test_compaction_reports_the_moves_it_needs_and_changes_nothing_without_room():
+    a = sa.SegmentAllocator(20)
+    m = AllocatorModel(20)
+    for r, n in ((1, 3), (2, 3), (1, 2), (2, 2)):
+        a.grow(r, n)
+        m.grow(r, n)
+    lib = sa._load()
+    cnt = ctypes.c_int64(-1)
+    moves = np.zeros((3, 4), dtype=np.int32)  # 4 needed
+    st = lib.seg_attn_allocator_compact(a._h, moves.ctypes.data, 3, ctypes.byref(cnt))
+    assert st == 3 and cnt.value == 4
+    _same_state(a, m, [1, 2])  # unchanged
+    got = a.compact()
+    assert got.tolist() == [[0, 10, 3, 0], [6, 13, 2, 3], [3, 15, 3, 5], [8, 18, 2, 8]]
+    m.compact()
+    _same_state(a, m, [1, 2])
+    assert lib.seg_attn_allocator_compact(None, None, 0, None) == 1

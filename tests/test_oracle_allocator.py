@@ -194,3 +194,98 @@ def test_in_place_extension_is_taken_whenever_possible():
         # the old last segment grew by min(n, room) and nothing else changed before it
         assert after[:len(segs) - 1] == segs[:-1]
         assert after[len(segs) - 1] == (segs[-1][0], segs[-1][1] + min(n, room))
+
+
+# ---------------------------------------------------------------- compaction
+
+from oracle.allocator import apply_moves
+
+
+def test_compaction_hand_worked():
+    # A: [0,3) then [6,8); B: [3,6) then [8,10); free [10,20). Both have two ranges, so A goes
+    # first (lower id) into [10,15), B into the rest [15,20); the old ranges free [0,10).
+    a = AllocatorModel(20)
+    assert a.grow(1, 3) and a.grow(2, 3) and a.grow(1, 2) and a.grow(2, 2)
+    assert a.owned(1) == [(0, 3), (6, 2)] and a.owned(2) == [(3, 3), (8, 2)]
+    moves = a.compact()
+    assert moves == [(0, 10, 3), (6, 13, 2), (3, 15, 3), (8, 18, 2)]
+    assert a.owned(1) == [(10, 5)] and a.owned(2) == [(15, 5)]
+    assert a.free_runs() == [(0, 10)]
+    assert a.compact() == []  # nothing fragmented any more
+
+
+def test_compaction_leaves_requests_that_fit_nowhere_and_copies_keys_only():
+    # free space of 2 slots: neither 5-slot request fits, nothing changes
+    a = AllocatorModel(12)
+    assert a.grow(1, 3) and a.grow(2, 3) and a.grow(1, 2) and a.grow(2, 2)
+    before = (a.owned(1), a.owned(2), a.free_runs())
+    assert a.compact() == []
+    assert (a.owned(1), a.owned(2), a.free_runs()) == before
+    # a request with 3 ranges goes before one with 2; spare capacity is not copied; a request
+    # with capacity but no keys moves without any copy
+    a = AllocatorModel(40)
+    assert a.grow(1, 2) and a.grow(2, 2) and a.grow(1, 2) and a.grow(2, 2) and a.grow(1, 2)
+    # 1: [0,2) [4,6) [8,10); 2: [2,4) [6,8); free [10,40)
+    assert a.reserve(1, 9)  # 3 more slots for request 1: in place after [8,10) -> [8,13)
+    assert a.owned(1) == [(0, 2), (4, 2), (8, 5)] and a.length(1) == 6
+    assert a.reserve(3, 2) and a.reserve(2, 4) is True  # 3 takes [13,15)
+    assert a.grow(4, 1) and a.reserve(3, 3)  # 4 takes [15,16); 3 gets [16,17) as a 2nd range
+    assert a.owned(3) == [(13, 2), (16, 1)] and a.length(3) == 0
+    moves = a.compact()
+    # 1 (3 ranges, capacity 9) -> [17, 26): copies its 6 keys; then 2 -> [26, 30); then 3 ->
+    # [30, 33) with nothing to copy
+    assert moves == [(0, 17, 2), (4, 19, 2), (8, 21, 2), (2, 26, 2), (6, 28, 2)]
+    assert a.owned(1) == [(17, 9)] and a.owned(2) == [(26, 4)] and a.owned(3) == [(30, 3)]
+    assert a.segments(1) == [(17, 6)] and a.length(3) == 0
+
+
+def test_compaction_keeps_every_key_and_moves_only_between_disjoint_ranges():
+    rng = np.random.default_rng(21)
+    for trial in range(30):
+        pool = int(rng.integers(200, 600))
+        a = AllocatorModel(pool, granule=int(rng.choice([1, 4, 16])))
+        for _ in range(int(rng.integers(20, 120))):
+            r = int(rng.integers(0, 10))
+            op = rng.random()
+            if op < 0.7:
+                a.grow(r, int(rng.integers(0, 25)))
+            elif op < 0.8:
+                a.reserve(r, int(rng.integers(0, 60)))
+            elif op < 0.9:
+                a.release(r)
+            else:
+                a.truncate(r, int(rng.integers(0, a.length(r) + 1)))
+        # label every key slot with (request, key index); other slots -1
+        label = np.full(pool, -1, dtype=np.int64)
+        reqs = sorted(a.segs)
+        for r in reqs:
+            i = 0
+            for off, ln in a.segments(r):
+                label[off:off + ln] = r * 10000 + np.arange(i, i + ln)
+                i += ln
+        used_before = a.used.copy()
+        frag_before = {r: len(a.owned(r)) for r in reqs}
+        caps = {r: a.capacity(r) for r in reqs}
+        moves = a.compact()
+        # destinations lie in space that was free; sources in space that was owned; no two
+        # ranges of the list (sources and destinations together) share a slot
+        cover = np.zeros(pool, dtype=np.int64)
+        for src, dst, n in moves:
+            assert not used_before[dst:dst + n].any() and used_before[src:src + n].all()
+            cover[src:src + n] += 1
+            cover[dst:dst + n] += 1
+        assert cover.max(initial=0) <= 1
+        after = apply_moves(label, moves)
+        for r in reqs:
+            assert a.capacity(r) == caps[r]
+            got = np.concatenate([after[o:o + n] for o, n in a.segments(r)] or [np.zeros(0, np.int64)])
+            assert np.array_equal(got, r * 10000 + np.arange(a.length(r)))
+            if len(a.owned(r)) > 1:  # not relocated: it fitted nowhere, or had one range
+                assert frag_before[r] == len(a.owned(r))
+        # the bitmap still equals the union of the owned ranges
+        owned = np.zeros(pool, dtype=bool)
+        for r in reqs:
+            for o, n in a.owned(r):
+                assert not owned[o:o + n].any()
+                owned[o:o + n] = True
+        assert np.array_equal(owned, a.used)
