@@ -20,14 +20,17 @@
 // A unit that covers a whole request writes the output; otherwise it writes a partial
 // (O_s, LSE_s) for the merge pass.
 //
-// FP8 pools (OCP E4M3FN codes with one fp32 scale per token and kv head) and INT8 pools
+// FP8 pools (OCP E4M3FN codes with one fp32 scale per token and kv head) are converted to bf16
+// exactly on the way into the MFMAs (every E4M3FN value is a bf16 value); INT8 pools
 // (two's-complement codes, same scales; the INT8 KV cache of "FlashAttention on Ascend NPU",
-// optimisation 3) are converted to bf16 exactly on the way into the MFMAs (every E4M3FN value
-// and every integer of magnitude <= 256 is a bf16 value); the key scale multiplies the scores,
-// the value scale the probabilities, so the arithmetic equals bf16 attention over the
-// dequantised pool.
+// optimisation 3) to f16, also exactly, with f16 MFMAs and Q widened to f16 (a conversion of four
+// codes costs five instructions, against ten for bf16). The key scale multiplies the scores, the
+// value scale the probabilities before their rounding to the operand type, so the arithmetic is
+// attention over the dequantised pool with the probabilities rounded to bf16 (f16 for INT8).
 //
 // Merge pass: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s per (request, head).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace segattn {
@@ -67,26 +70,70 @@ struct DecodeCfg<1> {  // fp8 / int8: 64 keys per wave tile, 128 B rows, + k/v s
 template <>
 struct DecodeCfg<2> : DecodeCfg<1> {};
 
-// 8 one-byte codes (bytes 0..3 of lo, then of hi) as 8 exact bf16 values.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// MFMA operand type of a pool format: bf16 for bf16 and FP8 pools (every E4M3FN value is a bf16
+// value), f16 for INT8 pools (every integer of magnitude <= 1024 is an f16 value, and the
+// conversion below is two instructions per 4 codes' worth of halves).
 template <int kKv>
-__device__ __forceinline__ bf16x8 codes8_to_bf16x8(uint32_t lo, uint32_t hi) {
+using OpT = typename std::conditional<kKv == 2, f16x8, bf16x8>::type;
+
+__device__ __forceinline__ f32x4 mfma_op(bf16x8 a, bf16x8 b, f32x4 c) { return mfma16x16x32(a, b, c); }
+__device__ __forceinline__ f32x4 mfma_op(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 4 two's-complement codes (one dword) as 4 exact f16 values: u = c + 128 is the code with its
+// top bit flipped; the half with bits 0x64 | u, that is 1024 + u, minus 1152 is c exactly.
+__device__ __forceinline__ void int8x4_to_f16(uint32_t w, f16x2& a, f16x2& b) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // bytes u0, 64, u1, 64
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // bytes u2, 64, u3, 64
+  const f16x2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  a = __builtin_bit_cast(f16x2, lo) + off;
+  b = __builtin_bit_cast(f16x2, hi) + off;
+}
+
+// 8 one-byte codes (bytes 0..3 of lo, then of hi) as 8 exact MFMA operand values.
+template <int kKv>
+__device__ __forceinline__ OpT<kKv> codes8_to_op(uint32_t lo, uint32_t hi) {
   if constexpr (kKv == 1) {
     return fp8x8_to_bf16x8(lo, hi);
   } else {
-    // int8 -> fp32 is exact and so is the fp32 -> bf16 truncation for |c| <= 128: the value
-    // has at most 8 significant bits
-    uint32_t w[4];
+    f16x2 r[4];
+    int8x4_to_f16(lo, r[0], r[1]);
+    int8x4_to_f16(hi, r[2], r[3]);
+    return __builtin_bit_cast(f16x8, r);
+  }
+}
+
+// Eight fp32 values as MFMA operands: bf16 (round to nearest even), or f16 (round to nearest
+// even) for the INT8 path.
+template <int kKv>
+__device__ __forceinline__ OpT<kKv> to_op8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                           float a6, float a7) {
+  if constexpr (kKv == 2) {
+    f16x8 r;
+    r[0] = (_Float16)a0; r[1] = (_Float16)a1; r[2] = (_Float16)a2; r[3] = (_Float16)a3;
+    r[4] = (_Float16)a4; r[5] = (_Float16)a5; r[6] = (_Float16)a6; r[7] = (_Float16)a7;
+    return r;
+  } else {
+    return to_bf16x8(a0, a1, a2, a3, a4, a5, a6, a7);
+  }
+}
+
+// Q (bf16 in LDS) as an operand: unchanged, or widened to f16 for the INT8 path (exact for every
+// bf16 value of f16's normal range; smaller ones round to f16 subnormals, below 2^-24 absolute).
+template <int kKv>
+__device__ __forceinline__ OpT<kKv> q_to_op(bf16x8 q) {
+  if constexpr (kKv == 2) {
+    f16x8 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t src = i < 2 ? lo : hi;
-      const int sh = 16 * (i & 1);
-      const float f0 = (float)(int)(int8_t)(src >> sh);
-      const float f1 = (float)(int)(int8_t)(src >> (sh + 8));
-      // high halves of the two floats: bytes 2, 3 of f0 then bytes 2, 3 of f1
-      w[i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0),
-                                   0x07060302u);
-    }
-    return __builtin_bit_cast(bf16x8, w);
+    for (int i = 0; i < 8; ++i) r[i] = (_Float16)(float)q[i];
+    return r;
+  } else {
+    return q;
   }
 }
 template <int kKv>
@@ -718,7 +765,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   };
 
   // ---- compute side
-  bf16x8 qf[4];  // B operand of S^T: lane holds d = 32*step + 8*grp + (0..7) of head `col`
+  OpT<kKv> qf[4];  // B operand of S^T: lane holds d = 32*step + 8*grp + (0..7) of head `col`
   f32x4 o[8];
   float m_run, l_run;
   auto reset = [&]() __attribute__((always_inline)) {
@@ -745,10 +792,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         : "v"(a)
         : "memory");
     const bool real = col < kGroup;
-    qf[0] = real ? __builtin_bit_cast(bf16x8, v0) : bf16x8{};
-    qf[1] = real ? __builtin_bit_cast(bf16x8, v1) : bf16x8{};
-    qf[2] = real ? __builtin_bit_cast(bf16x8, v2) : bf16x8{};
-    qf[3] = real ? __builtin_bit_cast(bf16x8, v3) : bf16x8{};
+    qf[0] = q_to_op<kKv>(real ? __builtin_bit_cast(bf16x8, v0) : bf16x8{});
+    qf[1] = q_to_op<kKv>(real ? __builtin_bit_cast(bf16x8, v1) : bf16x8{});
+    qf[2] = q_to_op<kKv>(real ? __builtin_bit_cast(bf16x8, v2) : bf16x8{});
+    qf[3] = q_to_op<kKv>(real ? __builtin_bit_cast(bf16x8, v3) : bf16x8{});
   };
 
   // Combine the 4 waves' states for unit r and write the output or the partial.
@@ -834,7 +881,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       const int r = 16 * mt + col;
 #pragma unroll
       for (int stp = 0; stp < 4; ++stp) {
-        bf16x8 a;
+        OpT<kKv> a;
         if constexpr (kKv == 0) {
           const int c = 4 * stp + grp;  // d = 32*stp + 8*grp
           a = lds_read16(kb + r * 256 + ((c ^ (r & 15)) << 4));
@@ -843,9 +890,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
           const int c = byte >> 4;
           const __attribute__((address_space(3))) uint32_t* p =
               (const __attribute__((address_space(3))) uint32_t*)(kb + r * 128 + ((c ^ (r & 7)) << 4) + (byte & 15));
-          a = codes8_to_bf16x8<kKv>(p[0], p[1]);
+          a = codes8_to_op<kKv>(p[0], p[1]);
         }
-        s[mt] = mfma16x16x32(a, qf[stp], s[mt]);
+        s[mt] = mfma_op(a, qf[stp], s[mt]);
       }
     }
     if constexpr (kKv != 0) {
@@ -907,17 +954,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       uint32_t v8lo[8], v8hi[8];
       if constexpr (kKv == 0) v_transposed(vb, kk, vt);
       else v_transposed8(vb, kk, v8lo, v8hi);
-      bf16x8 pb = to_bf16x8(s[2 * kk][0], s[2 * kk][1], s[2 * kk][2], s[2 * kk][3], s[2 * kk + 1][0],
-                            s[2 * kk + 1][1], s[2 * kk + 1][2], s[2 * kk + 1][3]);
+      const OpT<kKv> pb = to_op8<kKv>(s[2 * kk][0], s[2 * kk][1], s[2 * kk][2], s[2 * kk][3],
+                                      s[2 * kk + 1][0], s[2 * kk + 1][1], s[2 * kk + 1][2],
+                                      s[2 * kk + 1][3]);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        bf16x8 a;
+        OpT<kKv> a;
         if constexpr (kKv == 0) {
           a = vt[dt];
         } else {
-          a = codes8_to_bf16x8<kKv>(v8lo[dt], v8hi[dt]);
+          a = codes8_to_op<kKv>(v8lo[dt], v8hi[dt]);
         }
-        o[dt] = mfma16x16x32(a, pb, o[dt]);
+        o[dt] = mfma_op(a, pb, o[dt]);
       }
     }
   };
