@@ -51,6 +51,18 @@ constexpr float kRescaleLog2 = 8.0f;
 
 __device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// A block's pool rows as a raw buffer whose base is the block's first row (a scalar 64-bit add
+// per block): every lane's row offset is then a 32-bit register added by the load itself, with
+// no 64-bit address arithmetic on the vector ALU, and the LDS destination (M0) is scalar.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+// 16 bytes per lane from the buffer at byte offset voff into LDS: lane L's bytes land at
+// lds_base + 16 * L.
+__device__ __forceinline__ void copy16_buf(__amdgpu_buffer_rsrc_t r, lds_void_t* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
+}
+
 // Scalar cursor over a request's segments; every value is the same in all lanes.
 struct BlockCursor {
   const Segment* segs;
@@ -217,9 +229,9 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     kcur.advance_to(kb0);
     lds_char_t* l = (lds_char_t*)dst + wave * 2048;
     if ((kb0 + kBlockN <= K) && (last - kcur.start < kcur.len)) {
-      const char* base = (const char*)(kbase + ((int64_t)kcur.off + (kb0 - kcur.start)) * tok_stride);
+      const auto r = block_rsrc(kbase + ((int64_t)kcur.off + (kb0 - kcur.start)) * tok_stride);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) copy16_to_lds(base + koff[i], (lds_void_t*)(l + 1024 * i));
+      for (int i = 0; i < 2; ++i) copy16_buf(r, (lds_void_t*)(l + 1024 * i), koff[i]);
     } else {
       SegCursor c2;
       c2.segs = kcur.segs; c2.idx = kcur.idx; c2.end = kcur.end;
@@ -239,9 +251,9 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     vcur.advance_to(kb0);
     lds_char_t* l = (lds_char_t*)dst + vdst0;
     if ((kb0 + kBlockN <= K) && (last - vcur.start < vcur.len)) {
-      const char* base = (const char*)(vbase + ((int64_t)vcur.off + (kb0 - vcur.start)) * tok_stride);
+      const auto r = block_rsrc(vbase + ((int64_t)vcur.off + (kb0 - vcur.start)) * tok_stride);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) copy16_to_lds(base + voff[i], (lds_void_t*)(l + 1024 * i));
+      for (int i = 0; i < 2; ++i) copy16_buf(r, (lds_void_t*)(l + 1024 * i), voff[i]);
     } else {
       SegCursor c2;
       c2.segs = vcur.segs; c2.idx = vcur.idx; c2.end = vcur.end;
@@ -549,13 +561,12 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
     lds_char_t* lv = (lds_char_t*)vdst + wave * 4096;
     if ((kb0 + kBlockN <= K) && (last - cur.start < cur.len)) {
       const int64_t base = (int64_t)cur.off + (kb0 - cur.start);
-      const char* kb = (const char*)(kbase + base * tok_stride);
-      const char* vb = (const char*)(vbase + base * tok_stride);
+      const auto kr = block_rsrc(kbase + base * tok_stride);
+      const auto vr = block_rsrc(vbase + base * tok_stride);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) copy16_to_lds(kb + koff[k], (lds_void_t*)(lk + 1024 * k));
+      for (int k = 0; k < 4; ++k) copy16_buf(kr, (lds_void_t*)(lk + 1024 * k), koff[k]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        copy16_to_lds(vb + (size_t)(16 * k) * tok_bytes + voff, (lds_void_t*)(lv + 1024 * k));
+      for (int k = 0; k < 4; ++k) copy16_buf(vr, (lds_void_t*)(lv + 1024 * k), voff + (uint32_t)(16 * k) * tok_bytes);
     } else {
       SegCursor c2;
       c2.segs = cur.segs;
