@@ -11,9 +11,11 @@
 // The group loads its row (8 values per lane, 16-byte pieces), finds the token's request and
 // the key's pool slot with its lanes working together on the tables, and stores the row there.
 // The FP8 row scale is max|x| / 448 (1 for an all-zero row); each value is divided by it in
-// fp32, correctly rounded, and converted to E4M3FN by the hardware conversion (round to
-// nearest, ties to even) after a clamp to +-448. INT8 is the same with 127 in place of 448 and
-// a rounding to the nearest integer, ties to even.
+// fp32, correctly rounded, clamped to +-448 and converted to E4M3FN (round to nearest, ties to
+// even). INT8 is the same with 127 in place of 448 and a rounding to the nearest integer, ties
+// to even. The kernels reach the same bits by cheaper means: both divisions are replaced by
+// sequences that give the same scale and the same codes for every bf16 input, and the clamp is
+// left out where it cannot change a code (below).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,26 +31,29 @@ struct Seg {
 };
 
 constexpr int kRowsPerBlock = 16;
-constexpr float kFp8Max = 448.0f;
-constexpr float kInt8Max = 127.0f;
 
-// float pair -> two E4M3FN bytes in the low half of a word (hardware conversion, RNE)
-__device__ __forceinline__ uint32_t pack_fp8x2(float a, float b) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+// The row scale RN(a / M) for a bf16 row maximum a > 0: s0 = a c with c = RN(1 / M), then one
+// residual step s0 - (s0 M - a) c, the residual exact in an fma. Equal to the correctly
+// rounded quotient for every positive finite bf16 a, for M = 448 and M = 127 (checked
+// exhaustively over the 32640 values).
+template <int kM>
+__device__ __forceinline__ float row_scale(float a) {
+  constexpr float c = 1.0f / (float)kM;
+  const float s0 = a * c;
+  return __builtin_fmaf(-__builtin_fmaf(s0, (float)kM, -a), c, s0);
 }
 
-// x / s correctly rounded, from r = 1/s correctly rounded: q = x r, then two corrections
-// q -= (q s - x) r, each residual exact in an fma. After the first correction q is within one
-// ulp of x / s, and then the residual step rounds correctly (Markstein's theorem on division by
-// a correctly rounded reciprocal; it needs no underflow in the residuals, which the callers'
-// range of s, 2^-80 .. 2^80, ensures for every quotient of magnitude 2^-11 or more, and smaller
-// quotients encode as a signed zero either way). Written with the negated residual so that
-// x = -0 keeps its sign: (q s - x) is then +0 and -0 - (+0) r stays -0.
+// The code of x / s, from any reciprocal r within one ulp of 1 / s (the hardware reciprocal):
+// q = x r, then one residual step q - (q s - x) r. For a bf16 x with |x| <= a, the row's bf16
+// maximum, and s = RN(a / M) in [2^-80, 2^80], q may differ from the correctly rounded quotient
+// in its last bit, but never across a rounding boundary of the code: its E4M3FN code (M = 448)
+// or its nearest integer (M = 127) equals that of the correctly rounded quotient. Checked
+// exhaustively, every such (x, a) pair and each of the three reciprocals RN(1 / s) and its two
+// neighbours; a second residual step (Markstein's correctly rounded division) would change no
+// code. Written with the negated residual so that x = -0 keeps its sign.
 __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
-  float q = __fmul_rn(x, r);
-  q = __builtin_fmaf(-__builtin_fmaf(q, s, -x), r, q);
-  q = __builtin_fmaf(-__builtin_fmaf(q, s, -x), r, q);
-  return q;
+  const float q = __fmul_rn(x, r);
+  return __builtin_fmaf(-__builtin_fmaf(q, s, -x), r, q);
 }
 
 // Lane data movement inside the 16-lane DPP rows, which are the row groups: kCtrl is a DPP
@@ -87,30 +92,35 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4 raw, float (&x)[8]) {
   }
 }
 
-// Eight quotients, clamped to +-448, as E4M3FN codes (byte i = value i).
+// No clamp is needed before either encoding: with |x| <= a and s = RN(a / M) >= (a / M)(1 - 2^-24)
+// every quotient has |q| <= M (1 + 2^-22), which still rounds to +-M.
+
+// Eight quotients as E4M3FN codes (byte i = value i): the hardware conversion, two values per
+// instruction, the second pair into the high half of the word.
 __device__ __forceinline__ u32x2 encode_fp8x8(const float (&y)[8]) {
   uint32_t w[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    float c[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) c[q] = fminf(fmaxf(y[4 * i + q], -kFp8Max), kFp8Max);
-    w[i] = pack_fp8x2(c[0], c[1]) | (pack_fp8x2(c[2], c[3]) << 16);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * i], y[4 * i + 1], 0, false);
+    w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * i + 2], y[4 * i + 3], lo, true);
   }
   return u32x2{w[0], w[1]};
 }
 
-// Eight quotients, clamped to +-127, rounded to the nearest integer (ties to even), as
-// two's-complement bytes (byte i = value i).
+// Eight quotients rounded to the nearest integer (ties to even), as two's-complement bytes
+// (byte i = value i). Adding 1.5 * 2^23 rounds a float of magnitude below 2^22 to an integer
+// in the fp32 addition itself (round to nearest even), and the sum's low byte is that integer
+// modulo 256; byte permutes gather the four low bytes of a word.
 __device__ __forceinline__ u32x2 encode_int8x8(const float (&y)[8]) {
   uint32_t w[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     uint32_t b[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      b[q] = (uint32_t)(int)__builtin_rintf(fminf(fmaxf(y[4 * i + q], -kInt8Max), kInt8Max)) & 0xFFu;
-    w[i] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    for (int q = 0; q < 4; ++q) b[q] = __builtin_bit_cast(uint32_t, y[4 * i + q] + 0x1.8p23f);
+    const uint32_t p01 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // b0.byte0, b1.byte0
+    const uint32_t p23 = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+    w[i] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
   }
   return u32x2{w[0], w[1]};
 }
@@ -185,13 +195,13 @@ __device__ __forceinline__ void quantise_row_pair(const u32x4 kraw, const u32x4 
     }
     ak = group_max_nonneg(ak);
     av = group_max_nonneg(av);
-    constexpr float kMax = kFmt == 1 ? kFp8Max : kInt8Max;
-    const float sk = ak > 0.f ? ak / kMax : 1.0f;
-    const float sv = av > 0.f ? av / kMax : 1.0f;
+    constexpr int kM = kFmt == 1 ? 448 : 127;
+    const float sk = ak > 0.f ? row_scale<kM>(ak) : 1.0f;
+    const float sv = av > 0.f ? row_scale<kM>(av) : 1.0f;
     float yk[8], yv[8];
     auto in_range = [](float s) { return s >= 0x1p-80f && s <= 0x1p80f; };
     if (in_range(sk) && in_range(sv)) {  // the same for the whole group
-      const float rk = 1.0f / sk, rv = 1.0f / sv;
+      const float rk = __builtin_amdgcn_rcpf(sk), rv = __builtin_amdgcn_rcpf(sv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         yk[i] = div_by_scale(xk[i], sk, rk);
