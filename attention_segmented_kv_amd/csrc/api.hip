@@ -33,6 +33,11 @@ hipError_t launch_linear_prefill(const void* q, const void* k, const void* v, co
                                  const int32_t* cu, const int32_t* slots, int batch, int heads,
                                  float scale, int initial_state, float* pool, int64_t pool_slots,
                                  void* out, hipStream_t stream);
+int linear_fused_max_len();
+hipError_t launch_linear_prefill_fused(const void* q, const void* k, const void* v, const float* g,
+                                       const int32_t* cu, const int32_t* slots, int batch, int heads,
+                                       int max_len, float scale, int initial_state, float* pool,
+                                       int64_t pool_slots, void* out, hipStream_t stream);
 hipError_t launch_linear_decode(const void* q, const void* k, const void* v, const float* g,
                                 const int32_t* slots, int batch, int heads, float scale, float* pool,
                                 int64_t pool_slots, void* out, hipStream_t stream);
@@ -101,6 +106,13 @@ bool plan_decode(int batch, int max_k, int one_byte, int requested, DecodePlan* 
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// SEG_ATTN_LINEAR_PREFILL=chunked keeps the chunk-parallel linear prefill for short requests too
+// (tests use it to cover both paths); =fused, or unset, takes the closed form up to its length.
+bool linear_chunked_forced() {
+  const char* v = std::getenv("SEG_ATTN_LINEAR_PREFILL");
+  return v != nullptr && std::strcmp(v, "chunked") == 0;
+}
 
 // SEG_ATTN_PREFILL_TILE=128 or 256 pins the prefill tiling (tests use it to cover both).
 int prefill_tile_override() {
@@ -451,6 +463,10 @@ seg_attn_status_t seg_attn_linear_prefill(const void* q, const void* k, const vo
     if (workspace == nullptr) {
       e = segattn::launch_linear_prefill(q, k, v, g, cu_seqlens, state_slots, batch, num_heads, scale,
                                          initial_state, state_pool, pool_slots, out, (hipStream_t)stream);
+    } else if (max_seqlen <= segattn::linear_fused_max_len() && !linear_chunked_forced()) {
+      e = segattn::launch_linear_prefill_fused(q, k, v, g, cu_seqlens, state_slots, batch, num_heads,
+                                               max_seqlen, scale, initial_state, state_pool, pool_slots,
+                                               out, (hipStream_t)stream);
     } else {
       const int64_t maxc = ((int64_t)max_seqlen + 63) / 64;
       if ((int64_t)batch * maxc * num_heads * 2 > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;

@@ -95,6 +95,18 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // bits 3:0 and 15:14).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
+// A block's pool rows as a raw buffer whose base is the block's first row (a scalar 64-bit add
+// per block): every lane's row offset is then a 32-bit register added by the load itself, with
+// no 64-bit address arithmetic on the vector ALU, and the LDS destination (M0) is scalar.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+// 16 bytes per lane from the buffer at byte offset voff into LDS: lane L's bytes land at
+// lds_base + 16 * L.
+__device__ __forceinline__ void copy16_buf(__amdgpu_buffer_rsrc_t r, lds_void_t* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
+}
+
 // Transposing LDS read: within each group of 16 lanes, lane i receives element (i % 4) of the
 // 4 bf16 values addressed by lane 4 * jj + i / 4, for jj = 0..3.
 __device__ __forceinline__ bf16x4 lds_read_tr16(const lds_char_t* p) {

@@ -621,6 +621,515 @@ __global__ __launch_bounds__(kLaThreads) void la_chunk_out_kernel(
   }
 }
 
+// ------------------------------------------------------------ fused prefill (closed form)
+//
+// For requests of up to kFusedMaxLen tokens one launch computes the outputs and the final states
+// from the closed form of the recurrence, with G_t = g_0 + ... + g_t the decay sum from the
+// request's first token:
+//   o_t = scale * ( exp(G_t) q_t S_0 + sum_{s <= t} (q_t . k_s) exp(G_t - G_s) v_s )
+//   S_n = exp(G_{n-1}) S_0 + sum_s exp(G_{n-1} - G_s) k_s^T v_s
+// The cost grows with the square of the length, as causal attention's does, where the chunked
+// form's grows linearly; but no state is carried from chunk to chunk, so every term can be
+// computed at once, without a scan and without a workspace. Both sums are split over the waves
+// of a workgroup by key blocks, and since the terms simply add (no normalisation) the waves'
+// partial sums are added through LDS at the end. Workgroups of 8 waves:
+//   output workgroups, one per (64-query tile, request, head), heaviest tile first: wave w takes
+//     the 32 queries 32 (w / 4) .. + 31 of the tile and the 32-key blocks w % 4, w % 4 + 4, ...;
+//     the two waves with the same w % 4 share each block, copied once into LDS (K row-major and
+//     V, read back transposed), one workgroup barrier per step;
+//   state workgroups, four per (request, head), one per 64 x 64 quarter of the state: wave w
+//     takes the 32-key blocks w, w + 8, ... on its own (no barrier in the key loop), K scaled by
+//     its decay weight on the way into LDS.
+// Each workgroup forms the decay sums it needs by a prefix sum over the request's g (at most
+// kFusedMaxLen values) into LDS. With a stored initial state the state workgroups run in a second
+// launch, after every output workgroup has read S_0 from the slot they overwrite.
+
+constexpr int kFusedMaxLen = 4096;
+constexpr int kFThreads = 256;                  // 4 waves
+constexpr int kFQ = 64;                         // queries per output tile
+constexpr int kNT = kFQ / 32;                   // 32-query halves of a tile
+constexpr int kFKB = 32;                        // keys per block
+constexpr int kFGOff = 131072;                  // key-block slots and the partial sums below
+constexpr int kFLds = kFGOff + kFusedMaxLen * 4 + 16;  // then the decay sums and 4 wave totals
+
+typedef __attribute__((address_space(3))) float lds_f32_t;
+typedef __attribute__((address_space(3))) f32x4v lds_f32x4_t;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+
+// Blocks of 256-byte rows (128 bf16): K with 16-byte chunk c of row r at c ^ (r % 16), read 16
+// bytes per lane along rows; V and S_0 with chunk c at c ^ 4 (r % 4), read transposed.
+__device__ __forceinline__ int ksw(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+__device__ __forceinline__ int vsw(int r, int c) { return r * 256 + ((c ^ ((r & 3) << 2)) << 4); }
+// Blocks of 128-byte rows (64 bf16), read transposed: chunk c of row r at c ^ 4 ((r / 2) % 2).
+__device__ __forceinline__ int hsw(int r, int c) { return r * 128 + ((c ^ (((r >> 1) & 1) << 2)) << 4); }
+
+// This lane's address for the transposing read of rows r0 + rstride * (lane / 32) + jj (jj =
+// 0..3) and columns 32 tile + lane % 32 of a vsw (wide) or hsw (half-width) block: after the read
+// the lane holds those four values of its column. Each group of 16 lanes reads 4 rows x 16
+// columns; over the wave the 64 pieces of 8 bytes fall on every 8-byte bank pair exactly twice.
+template <bool kHalf>
+__device__ __forceinline__ int tr_addr(int r0, int rstride, int tile) {
+  const int l = threadIdx.x & 63;
+  const int grp = l >> 4, jj = (l >> 2) & 3, u = l & 3;
+  const int r = r0 + rstride * (grp >> 1) + jj;
+  const int c = 4 * tile + 2 * (grp & 1) + (u >> 1);
+  return (kHalf ? hsw(r, c) : vsw(r, c)) + 8 * (u & 1);
+}
+
+// Two transposing reads, off_hi bytes apart, as one 8-value MFMA operand.
+__device__ __forceinline__ bf16x8 tr_pair(const lds_char_t* p, int off_hi) {
+  const bf16x4 lo = lds_read_tr16(p), hi = lds_read_tr16(p + off_hi);
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Gl[t] = log2(e) (g_0 + ... + g_t) for the request's tokens t < cnt of head h (cnt <=
+// kFusedMaxLen), in two parts so that the loads can be issued first and the scan done later:
+// decay_load gives each thread the running sums of its (up to 16) consecutive tokens, decay_scan
+// adds the totals of the threads before it and writes Gl; every thread of the workgroup takes
+// part, and decay_scan ends with a barrier.
+struct DecayPart {
+  float vals[16];
+};
+__device__ __forceinline__ void decay_load(const float* __restrict__ g, int t_begin, int H, int h, int cnt,
+                                           DecayPart& d) {
+  const int tid = threadIdx.x;
+  const int per = (cnt + kFThreads - 1) / kFThreads;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = tid * per + i;
+    d.vals[i] = (i < per && t < cnt) ? g[(int64_t)(t_begin + t) * H + h] : 0.f;
+  }
+}
+__device__ __forceinline__ void decay_scan(int cnt, DecayPart& d, lds_f32_t* Gl, lds_f32_t* wsum) {
+  const int tid = threadIdx.x;
+  const int per = (cnt + kFThreads - 1) / kFThreads;
+  float run = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    run += d.vals[i];
+    d.vals[i] = run;
+  }
+  const float incl = wave_inclusive_sum(run);
+  if ((tid & 63) == 63) wsum[tid >> 6] = incl;
+  __syncthreads();
+  float off = incl - run;
+  for (int w = 0; w < (tid >> 6); ++w) off += wsum[w];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = tid * per + i;
+    if (i < per && t < cnt) Gl[t] = (d.vals[i] + off) * kLog2e;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void sched_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void fused_outputs(
+    lds_char_t* lds, lds_f32_t* Gl, lds_f32_t* wsum, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ g,
+    int t_begin, int n, int H, int h, int j, int n_tiles, int64_t slot, float scale,
+    int initial_state, const float* __restrict__ pool, uint16_t* __restrict__ out) {
+  const int q0 = j * kFQ;
+  if (q0 >= n) return;  // the whole workgroup leaves together
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t hstride = (int64_t)H * kLaDim;
+  const int cnt = min(n, q0 + kFQ);  // keys the tile sees; also one past its last query
+  DecayPart dec;
+  decay_load(g, t_begin, H, h, cnt, dec);  // first: the decay sums are on the longest path
+  if (j == n_tiles - 1 && n > n_tiles * kFQ) {
+    // tokens past the covered length (a request longer than max_seqlen): NaN
+    const int first = n_tiles * kFQ;
+    for (int x = tid; x < (n - first) * 64; x += kFThreads)
+      *reinterpret_cast<uint32_t*>(out + (int64_t)(t_begin + first + x / 64) * hstride + h * kLaDim + 2 * (x % 64)) =
+          0x7FC07FC0u;
+  }
+
+  // Q^T (B operands of P^T = K Q^T) of the tile's two 32-query halves: lane holds
+  // q_t[16 step + 8 hh + 0..7] of query t = q0 + 32 nt + l32
+  bf16x8 qf[kNT][8];
+  int tq[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    tq[nt] = min(q0 + 32 * nt + l32, n - 1);
+    const uint16_t* qrow = q + (int64_t)(t_begin + tq[nt]) * hstride + h * kLaDim + 8 * hh;
+#pragma unroll
+    for (int step = 0; step < 8; ++step) qf[nt][step] = *reinterpret_cast<const bf16x8*>(qrow + 16 * step);
+  }
+
+  // ---- key blocks: wave w takes blocks w, w + 4, ... of the tile's keys, in two slots of its
+  // own (16 KiB each: K at +0, V at +8 KiB); no workgroup barrier in the loop
+  const int nkb = (cnt + kFKB - 1) / kFKB;
+  const int mine = nkb > wave ? (nkb - 1 - wave) / 4 + 1 : 0;
+  lds_char_t* slot0 = lds + wave * 32768;
+  lds_char_t* slot1 = slot0 + 16384;
+  const int cr = lane >> 4;  // copy instruction c fills rows 4 c + cr, chunk position lane % 16
+  const uint32_t rowb = (uint32_t)hstride * 2;
+  uint32_t kco[8];  // K: chunk (lane % 16) ^ (row % 16) of the row; V: chunk (lane % 16) ^ 4 cr
+#pragma unroll
+  for (int c = 0; c < 8; ++c) kco[c] = (uint32_t)((lane & 15) ^ ((4 * c + cr) & 15)) << 4;
+  const uint32_t vco = (uint32_t)((lane & 15) ^ (cr << 2)) << 4;
+  // Block kb's copies (rows 4 c + cr of K and of V, c = 0..7), from buffers based at the
+  // block's first row; rows past the tile's keys re-read its last key. copy_one(x) issues copy
+  // x (0..15) of the 16, so that they can be spread between the MFMAs.
+  struct Copies {
+    __amdgpu_buffer_rsrc_t kr, vr;
+    int lim;
+    lds_char_t* dst;
+  };
+  auto copies_of = [&](int kb, lds_char_t* dst) __attribute__((always_inline)) {
+    const int s0 = kb * kFKB;
+    const int64_t base = (int64_t)(t_begin + s0) * hstride + h * kLaDim;
+    return Copies{block_rsrc(k + base), block_rsrc(v + base), cnt - 1 - s0, dst};
+  };
+  auto copy_one = [&](const Copies& cp, int x) __attribute__((always_inline)) {
+    const int c = x >> 1;
+    const uint32_t ro = (uint32_t)min(4 * c + cr, cp.lim) * rowb;
+    if ((x & 1) == 0) copy16_buf(cp.kr, (lds_void_t*)(cp.dst + 1024 * c), ro + kco[c]);
+    else copy16_buf(cp.vr, (lds_void_t*)(cp.dst + 8192 + 1024 * c), ro + vco);
+  };
+
+  f32x16 o[4][kNT];
+#pragma unroll
+  for (int md = 0; md < 4; ++md)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) o[md][nt] = f32x16{};
+
+  if (initial_state) {
+    // exp(G_t) q_t S_0 for d_v tile `wave`, both query halves: S_0 as bf16 [128 i][128 d] (vsw)
+    // in the first 32 KiB, before any key block is copied there
+    const float* s0 = pool + (slot * H + h) * (int64_t)(kLaDim * kLaDim);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int qd = tid + kFThreads * c;
+      const int i = qd >> 4, ch = qd & 15;
+      const f32x4v a = *reinterpret_cast<const f32x4v*>(s0 + i * kLaDim + 8 * ch);
+      const f32x4v b = *reinterpret_cast<const f32x4v*>(s0 + i * kLaDim + 8 * ch + 4);
+      *(lds_bf16x8_t*)(lds + vsw(i, ch)) = to_bf16x8(a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]);
+    }
+    __syncthreads();
+    // A = S_0^T rows d, k = i in the order of qf: rows 16 st + 8 hh + jj, then + 4
+    const int a0 = tr_addr<false>(0, 8, wave);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 a = tr_pair(lds + a0 + 4096 * st, 1024);
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int md = 0; md < 4; ++md)
+          if (md == wave) o[md][nt] = mfma32x32x16(a, qf[nt][st], o[md][nt]);
+    }
+    __syncthreads();  // the key blocks below overwrite S_0; the exp(G_t) factor comes with G
+  }
+  if (mine > 0) {  // in flight during the decay sums
+    const Copies cp = copies_of(wave, slot0);
+#pragma unroll
+    for (int x = 0; x < 16; ++x) copy_one(cp, x);
+  }
+  decay_scan(cnt, dec, Gl, wsum);
+  float Gt[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) Gt[nt] = Gl[tq[nt]];
+  if (initial_state) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const float et = fast_exp2(Gt[nt]);
+#pragma unroll
+      for (int md = 0; md < 4; ++md)
+        if (md == wave) o[md][nt] *= et;
+    }
+  }
+
+  int kofs[8];
+#pragma unroll
+  for (int step = 0; step < 8; ++step) kofs[step] = ksw(l32, 2 * step + hh);
+  int vaddr[4];
+#pragma unroll
+  for (int md = 0; md < 4; ++md) vaddr[md] = 8192 + tr_addr<false>(0, 4, md);
+
+  // block kb from src; the next block's 16 copies (if nxt_kb >= 0) go out one after each MFMA of
+  // P^T = K Q^T, so that no copy instruction waits long for the memory pipeline (the wave issues
+  // in order) and they have the rest of the block to land
+  auto compute = [&](int kb, const lds_char_t* src, int nxt_kb, lds_char_t* nxt) __attribute__((always_inline)) {
+    bf16x8 kf[8];
+#pragma unroll
+    for (int step = 0; step < 8; ++step) kf[step] = lds_read16(src + kofs[step]);
+    const int s0 = kb * kFKB;
+    f32x4v gs[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) gs[g4] = *(const lds_f32x4_t*)(Gl + s0 + 8 * g4 + 4 * hh);
+    f32x16 p[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) p[nt] = f32x16{};
+    const Copies cp = copies_of(nxt_kb < 0 ? kb : nxt_kb, nxt);
+#pragma unroll
+    for (int step = 0; step < 8; ++step)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        p[nt] = mfma32x32x16(kf[step], qf[nt][step], p[nt]);
+        if (nxt_kb >= 0)
+#pragma unroll
+          for (int x = 0; x < 2 / kNT; ++x) copy_one(cp, (step * kNT + nt) * (2 / kNT) + x);
+      }
+    bf16x8 vf[4][2];
+#pragma unroll
+    for (int md = 0; md < 4; ++md) {
+      vf[md][0] = tr_pair(src + vaddr[md], 2048);
+      vf[md][1] = tr_pair(src + vaddr[md] + 4096, 2048);
+    }
+    // P^T[s][t] *= exp(G_t - G_s), s = s0 + 8 (e / 4) + 4 hh + e % 4; keys after t hidden
+    bf16x8 pb[kNT][2];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const int tw = q0 + 32 * nt;  // first query of the half
+      const bool diag = s0 + kFKB - 1 > tw;
+      const int t = tw + l32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = p[nt][e] * fast_exp2(Gt[nt] - gs[e >> 2][e & 3]);
+        p[nt][e] = (!diag || s0 + 8 * (e >> 2) + 4 * hh + (e & 3) <= t) ? pe : 0.f;
+      }
+      pb[nt][0] = to_bf16x8(p[nt][0], p[nt][1], p[nt][2], p[nt][3], p[nt][4], p[nt][5], p[nt][6], p[nt][7]);
+      pb[nt][1] = to_bf16x8(p[nt][8], p[nt][9], p[nt][10], p[nt][11], p[nt][12], p[nt][13], p[nt][14], p[nt][15]);
+    }
+#pragma unroll
+    for (int stp = 0; stp < 2; ++stp)
+#pragma unroll
+      for (int md = 0; md < 4; ++md)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) o[md][nt] = mfma32x32x16(vf[md][stp], pb[nt][stp], o[md][nt]);
+  };
+
+  // Double buffered per wave: block i + 1's copies are issued during block i's MFMAs, and block
+  // i + 1 is waited for (all copies done) just before it is used.
+  for (int i = 0; i < mine; ++i) {
+    sched_fence();
+    wait_vmem();
+    sched_fence();
+    const bool more = i + 1 < mine;
+    compute(wave + 4 * i, (i & 1) ? slot1 : slot0, more ? wave + 4 * (i + 1) : -1, (i & 1) ? slot0 : slot1);
+  }
+
+  // ---- add the 4 waves' partials through LDS; wave w finishes d_v tile w of all 64 queries
+  __syncthreads();
+  lds_f32x4_t* red = (lds_f32x4_t*)lds;  // [wave][md][nt][e / 4][lane]: 128 KiB
+#pragma unroll
+  for (int md = 0; md < 4; ++md)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        red[(((wave * 4 + md) * kNT + nt) * 4 + e4) * 64 + lane] =
+            f32x4v{o[md][nt][4 * e4], o[md][nt][4 * e4 + 1], o[md][nt][4 * e4 + 2], o[md][nt][4 * e4 + 3]};
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    const int t = q0 + 32 * nt + l32;
+    if (t >= n) continue;
+    uint16_t* orow = out + (int64_t)(t_begin + t) * hstride + h * kLaDim + 32 * wave + 4 * hh;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      f32x4v x = red[(((0 * 4 + wave) * kNT + nt) * 4 + e4) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) x += red[(((w * 4 + wave) * kNT + nt) * 4 + e4) * 64 + lane];
+      const uint32_t lo = float_to_bf16_bits(x[0] * scale) | (float_to_bf16_bits(x[1] * scale) << 16);
+      const uint32_t hi = float_to_bf16_bits(x[2] * scale) | (float_to_bf16_bits(x[3] * scale) << 16);
+      *reinterpret_cast<u32x2*>(orow + 8 * e4) = u32x2{lo, hi};
+    }
+  }
+}
+
+// One 64 x 64 quarter of a request's final state: d_v columns 64 dh .., d_k rows 64 ih ...
+__device__ __forceinline__ void fused_state(
+    lds_char_t* lds, lds_f32_t* Gl, lds_f32_t* wsum, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ g, int t_begin, int n, int H, int h,
+    int part, int max_len, int64_t slot, int initial_state, float* __restrict__ pool) {
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dh = part >> 1, ih = part & 1;
+  const int64_t hstride = (int64_t)H * kLaDim;
+  float* st = pool + (slot * H + h) * (int64_t)(kLaDim * kLaDim);
+  if (n > max_len) {  // a request longer than max_seqlen: its state is NaN
+    for (int x = tid; x < 64 * 64; x += kFThreads)
+      st[(64 * ih + (x >> 6)) * kLaDim + 64 * dh + (x & 63)] = __builtin_nanf("");
+    return;
+  }
+
+  // wave w: blocks w, w + 4, ... (block i of the wave: w + 4 i); V copies two blocks ahead into
+  // a ring of 3 slots of 4 KiB, K rows two blocks ahead in registers, scaled into one K~ slot
+  // (4 KiB) just before use: 16 KiB per wave
+  DecayPart dec;
+  decay_load(g, t_begin, H, h, n, dec);  // first: the decay sums are on the longest path
+  const int nkb = (n + kFKB - 1) / kFKB;
+  const int mine = nkb > wave ? (nkb - 1 - wave) / 4 + 1 : 0;
+  lds_char_t* wbase = lds + wave * 16384;
+  lds_char_t* ktl = wbase + 12288;
+  // K rows (64 d_k values, 128 bytes): copy c takes chunk (lane + 64 c) of the block, row
+  // (lane + 64 c) / 8; V rows: copy instruction c fills rows 8 c + lane / 8, position lane % 8.
+  u32x4 kreg[2][4];
+  const uint32_t rowb = (uint32_t)hstride * 2;
+  auto load_k = [&](int kb, u32x4 (&kr)[4]) __attribute__((always_inline)) {
+    const int lim = n - 1 - kb * kFKB;
+    const auto rs = block_rsrc(k + (int64_t)(t_begin + kb * kFKB) * hstride + h * kLaDim + 64 * ih);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int qd = lane + 64 * c;
+      kr[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)min(qd >> 3, lim) * rowb + 16 * (qd & 7), 0, 0);
+    }
+  };
+  auto dma_v = [&](int kb, lds_char_t* dst) __attribute__((always_inline)) {
+    const int lim = n - 1 - kb * kFKB;
+    const auto rs = block_rsrc(v + (int64_t)(t_begin + kb * kFKB) * hstride + h * kLaDim + 64 * dh);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int r = 8 * c + (lane >> 3);
+      const int ch = (lane & 7) ^ (((r >> 1) & 1) << 2);
+      copy16_buf(rs, (lds_void_t*)(dst + 1024 * c), (uint32_t)min(r, lim) * rowb + 16 * ch);
+    }
+  };
+  const int blk0 = wave, blk1 = wave + 4;
+  if (mine > 0) {
+    load_k(blk0, kreg[0]);
+    dma_v(blk0, wbase);
+  }
+  if (mine > 1) {
+    load_k(blk1, kreg[1]);
+    dma_v(blk1, wbase + 4096);
+  }
+  decay_scan(n, dec, Gl, wsum);
+  const float Gn = n > 0 ? Gl[n - 1] : 0.f;
+
+  // S^T partial [dt][it]: d = 64 dh + 32 dt + 8 (e / 4) + 4 hh + e % 4, i = 64 ih + 32 it + l32
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int it = 0; it < 2; ++it) acc[dt][it] = f32x16{};
+  int va[2], ka[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    va[x] = tr_addr<true>(0, 4, x);
+    ka[x] = tr_addr<true>(0, 4, x);
+  }
+  // K~[s] = exp(G_{n-1} - G_s) k_s, zero past the request (where V re-reads the last row)
+  auto store_k = [&](int kb, const u32x4 (&kr)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int qd = lane + 64 * c;
+      const int r = qd >> 3, s = kb * kFKB + r;
+      const float w = s < n ? fast_exp2(Gn - Gl[s]) : 0.f;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_bits_to_float(kr[c][e] & 0xFFFFu) * w;
+        x[2 * e + 1] = bf16_bits_to_float(kr[c][e] >> 16) * w;
+      }
+      *(lds_bf16x8_t*)(ktl + hsw(r, qd & 7)) = to_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    }
+  };
+  auto compute = [&](const lds_char_t* vsrc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int stp = 0; stp < 2; ++stp) {
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        a[x] = tr_pair(vsrc + va[x] + 2048 * stp, 1024);
+        b[x] = tr_pair(ktl + ka[x] + 2048 * stp, 1024);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int it = 0; it < 2; ++it) acc[dt][it] = mfma32x32x16(a[dt], b[it], acc[dt][it]);
+    }
+  };
+  // step i: K~ of block i from registers, block i + 2 requested (K into the registers just
+  // freed, V into the ring slot block i - 1 used), then block i's V waited for: 8 or 16
+  // operations of later blocks may still be in flight
+  auto step = [&](int i, u32x4 (&kr)[4]) __attribute__((always_inline)) {
+    const int kb = wave + 4 * i;
+    store_k(kb, kr);
+    const bool more2 = i + 2 < mine;
+    if (more2) {
+      load_k(kb + 8, kr);
+      dma_v(kb + 8, wbase + 4096 * ((i + 2) % 3));
+    }
+    sched_fence();
+    if (more2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+    else if (i + 1 < mine) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+    else wait_vmem();
+    sched_fence();
+    compute(wbase + 4096 * (i % 3));
+  };
+  for (int i = 0; i < mine; i += 2) {
+    step(i, kreg[0]);
+    if (i + 1 < mine) step(i + 1, kreg[1]);
+  }
+
+  // ---- add the 4 waves' partials through LDS; wave w finishes tile (w / 2, w % 2)
+  __syncthreads();
+  lds_f32x4_t* red = (lds_f32x4_t*)lds;  // [wave][tile][e / 4][lane]: 64 KiB
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        red[((wave * 4 + dt * 2 + it) * 4 + e4) * 64 + lane] =
+            f32x4v{acc[dt][it][4 * e4], acc[dt][it][4 * e4 + 1], acc[dt][it][4 * e4 + 2], acc[dt][it][4 * e4 + 3]};
+  __syncthreads();
+  {
+    const int dt = wave >> 1, it = wave & 1;
+    const int i = 64 * ih + 32 * it + l32;
+    const float en = fast_exp2(Gn);
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int d = 64 * dh + 32 * dt + 8 * e4 + 4 * hh;
+      f32x4v x = {0.f, 0.f, 0.f, 0.f};
+      if (initial_state) x = *reinterpret_cast<const f32x4v*>(st + i * kLaDim + d) * en;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x += red[((w * 4 + wave) * 4 + e4) * 64 + lane];
+      *reinterpret_cast<f32x4v*>(st + i * kLaDim + d) = x;
+    }
+  }
+}
+
+// roles: 1 = output workgroups, 2 = state workgroups (placed first in the grid), 3 = both.
+__global__ __launch_bounds__(kFThreads) void la_fused_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const int32_t* __restrict__ cu, const int32_t* __restrict__ slots,
+    int batch, int H, int max_len, int n_tiles, int roles, float scale, int initial_state,
+    float* __restrict__ pool, int64_t pool_slots, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kFLds];
+  lds_char_t* lds = (lds_char_t*)lds_raw;
+  lds_f32_t* Gl = (lds_f32_t*)(lds + kFGOff);
+  lds_f32_t* wsum = Gl + kFusedMaxLen;  // the 4 wave totals of the prefix sum
+  // workgroup order: the state workgroups (quarter-major), then output tiles heaviest first,
+  // (request, head) fastest throughout, so that with 8 | H every workgroup of head h runs on XCD
+  // h % 8 and shares its L2
+  const int bh_count = batch * H;
+  const int n_state = (roles & 2) ? 4 * bh_count : 0;
+  const int id = blockIdx.x;
+  const bool state_role = id < n_state;
+  const int bh = state_role ? id % bh_count : (id - n_state) % bh_count;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t slot = slots[b];
+  if (slot < 0 || slot >= pool_slots) return;  // the whole workgroup leaves together
+  const int t_begin = cu[b], n = cu[b + 1] - t_begin;
+  if (state_role) {
+    fused_state(lds, Gl, wsum, k, v, g, t_begin, n, H, h, id / bh_count, max_len, slot, initial_state, pool);
+  } else {
+    const int j = n_tiles - 1 - (id - n_state) / bh_count;
+    fused_outputs(lds, Gl, wsum, q, k, v, g, t_begin, n, H, h, j, n_tiles, slot, scale, initial_state,
+                  pool, out);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_linear_prefill(const void* q, const void* k, const void* v, const float* g,
@@ -673,6 +1182,29 @@ hipError_t launch_linear_prefill_parallel(const void* q, const void* k, const vo
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, g, cu, slots, heads, maxc,
                      scale, initial_state, pool_slots, sb, (uint16_t*)out);
   return hipGetLastError();
+}
+
+int linear_fused_max_len() { return kFusedMaxLen; }
+
+hipError_t launch_linear_prefill_fused(const void* q, const void* k, const void* v, const float* g,
+                                       const int32_t* cu, const int32_t* slots, int batch, int heads,
+                                       int max_len, float scale, int initial_state, float* pool,
+                                       int64_t pool_slots, void* out, hipStream_t stream) {
+  const int n_tiles = (max_len + kFQ - 1) / kFQ;
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh == 0) return hipSuccess;
+  auto go = [&](int roles) {
+    const int64_t grid = ((roles & 2) ? 4 * bh : 0) + ((roles & 1) ? bh * n_tiles : 0);
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(la_fused_kernel, dim3((unsigned)grid), dim3(kFThreads), 0, stream, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, g, cu, slots, batch, heads, max_len, n_tiles,
+                       roles, scale, initial_state, pool, pool_slots, (uint16_t*)out);
+    return hipGetLastError();
+  };
+  if (!initial_state) return go(3);
+  // the output workgroups read S_0 from the slots the state workgroups overwrite
+  const hipError_t e = go(1);
+  return e != hipSuccess ? e : go(2);
 }
 
 hipError_t launch_linear_decode(const void* q, const void* k, const void* v, const float* g,

@@ -159,7 +159,8 @@ def measure_linear(name, steps, warmup, dev):
         achieved = work / (us * 1e-6) / 1e12
         rf = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
               "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic("linear", name),
-              "note": "chunk-parallel: chunk states, a state scan, chunk outputs (three kernels)"}
+              "note": "one launch of the closed form (requests up to 4096 tokens); the unit counts "
+                      "the chunked form's flops"}
     else:
         achieved = work / (us * 1e-6) / 1e9
         rf = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -240,14 +240,24 @@ seg_attn_status_t seg_attn_kv_append(const void* k_new, const void* v_new,
  * out          [T, H, 128] bf16.
  * Prefill: request b's tokens are rows cu_seqlens[b] .. cu_seqlens[b+1]-1; its state starts
  * from its slot (initial_state = 1) or from zero (0) and the final state is written back to the
- * slot. Chunks of 64 tokens; the products run on bf16 operands with fp32 accumulation and an
- * fp32 state. With a workspace (of seg_attn_linear_prefill_workspace_bytes(batch, max_seqlen,
- * H, 128) bytes, 256-byte aligned, contents clobbered) all chunks of all requests run in
- * parallel, with a scan carrying the state between them; max_seqlen (HOST) must be at least every
- * request's length: a longer request is not processed past it, and its later tokens' outputs and
- * its final state are written as NaN so the broken bound shows. With workspace = NULL one
- * workgroup per (request, head, half of d_v) walks the chunks in order and max_seqlen is unused. Decode: one token per request (row b), state read from and written to the slot,
- * in fp32 throughout. Buffers: q, k, v and the pool 16-byte aligned, out 8-byte.
+ * slot. The products run on bf16 operands with fp32 accumulation and an fp32 state. Three
+ * evaluation orders of the same recurrence:
+ *   - workspace != NULL and max_seqlen <= 4096: one launch of the closed form
+ *     o_t = scale (exp(G_t) q_t S_0 + sum_{s<=t} (q_t . k_s) exp(G_t - G_s) v_s), G the running
+ *     sum of g, with the final state from the same sums; the workspace is not used (a stored
+ *     initial state takes a second launch, for the states, after the outputs have read S_0);
+ *   - workspace != NULL and longer requests: 64-token chunks of all requests in parallel, with a
+ *     scan carrying the state between them; the workspace must hold
+ *     seg_attn_linear_prefill_workspace_bytes(batch, max_seqlen, H, 128) bytes, 256-byte aligned
+ *     (contents clobbered); the environment variable SEG_ATTN_LINEAR_PREFILL=chunked selects this
+ *     order at every length;
+ *   - workspace = NULL: one workgroup per (request, head, half of d_v) walks the request's
+ *     64-token chunks in order; max_seqlen is unused.
+ * With a workspace, max_seqlen (HOST) must be at least every request's length: a longer request
+ * is not processed past it (rounded up to 64 tokens), and its later tokens' outputs and its
+ * final state are written as NaN so the broken bound shows.
+ * Decode: one token per request (row b), state read from and written to the slot, in fp32
+ * throughout. Buffers: q, k, v and the pool 16-byte aligned, out 8-byte.
  * Returns SEG_ATTN_OK, or an error before anything is launched.
  */
 seg_attn_status_t seg_attn_linear_prefill(const void* q, const void* k, const void* v,

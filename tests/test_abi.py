@@ -158,7 +158,8 @@ def _linear_args(**over):
     (dict(q=None), 1), (dict(pool=None), 1), (dict(cu=None), 1), (dict(batch=-1), 1), (dict(h=0), 1),
     (dict(d=64), 2), (dict(init=2), 1), (dict(scale=float("inf")), 1), (dict(npool=-1), 1),
     (dict(k=264), 1), (dict(out=260), 1), (dict(batch=0), 0), (dict(maxl=-1), 1),
-    (dict(ws=512, wsb=1024), 3), (dict(ws=520, wsb=1 << 40), 1),
+    # the workspace is checked where it is used: requests longer than the closed form's 4096
+    (dict(ws=512, wsb=1024, maxl=5000), 3), (dict(ws=520, wsb=1 << 40, maxl=5000), 1),
 ])
 def test_linear_prefill_rejects_bad_arguments(over, status):
     lib = _lib()

@@ -44,18 +44,36 @@ def _oracle(w, pool_before):
                                    w.cu_seqlens.cpu().numpy(), s0, w.scale)
 
 
-def _run(w, parallel=True):
+# Prefill paths: "fused" (the closed form, one launch; the default up to 4096 tokens),
+# "chunked" (chunk-parallel with a workspace; forced here through SEG_ATTN_LINEAR_PREFILL) and
+# "sequential" (no workspace).
+PATHS = ["fused", "chunked", "sequential"]
+
+
+@pytest.fixture
+def path_env(monkeypatch):
+    def use(path):
+        if path == "chunked":
+            monkeypatch.setenv("SEG_ATTN_LINEAR_PREFILL", "chunked")
+        else:
+            monkeypatch.delenv("SEG_ATTN_LINEAR_PREFILL", raising=False)
+    yield use
+    monkeypatch.delenv("SEG_ATTN_LINEAR_PREFILL", raising=False)
+
+
+def _run(w, path="fused"):
     sa = _sa()
     if w.kind == "decode":
         return sa.linear_decode(w.q, w.k, w.v, w.g, w.state_slots, w.state_pool, scale=w.scale)
     return sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool,
-                             initial_state=w.initial_state, scale=w.scale, parallel=parallel)
+                             initial_state=w.initial_state, scale=w.scale,
+                             parallel=path != "sequential")
 
 
-def _check(w, name, parallel=True):
+def _check(w, name, path="fused"):
     pool_before = w.state_pool.detach().cpu().clone()
     o_ref, st_ref = _oracle(w, pool_before)
-    out = _run(w, parallel)
+    out = _run(w, path)
     torch.cuda.synchronize()
     _assert_rel(out.float().cpu().numpy(), o_ref, name)
     pool_after = w.state_pool.detach().cpu()
@@ -71,14 +89,16 @@ def _check(w, name, parallel=True):
 
 
 @needs_gpu
-@pytest.mark.parametrize("parallel", [True, False], ids=["chunk-parallel", "sequential"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("initial_state", [False, True])
-def test_linear_prefill_ragged(initial_state, parallel):
-    """Lengths around the 64-token chunk: 1, 63, 64, 65, 130, an empty request."""
-    print(f"[case] linear prefill ragged initial_state={initial_state} parallel={parallel}", flush=True)
-    w = wl.make_linear(31, [1, 63, 64, 65, 130, 0], kind="prefill", initial_state=initial_state,
-                       num_heads=4).to("cuda")
-    _check(w, f"la-ragged-{int(initial_state)}-{int(parallel)}", parallel)
+def test_linear_prefill_ragged(initial_state, path, path_env):
+    """Lengths around the 32-token tile and the 64-token chunk: 1, 31, 33, 63, 64, 65, 130, an
+    empty request."""
+    path_env(path)
+    print(f"[case] linear prefill ragged initial_state={initial_state} path={path}", flush=True)
+    w = wl.make_linear(31, [1, 63, 64, 65, 130, 0, 31, 33], kind="prefill",
+                       initial_state=initial_state, num_heads=4).to("cuda")
+    _check(w, f"la-ragged-{int(initial_state)}-{path}", path)
 
 
 @needs_gpu
@@ -91,18 +111,38 @@ def test_linear_named_workloads(name):
 
 
 @needs_gpu
-def test_linear_sequential_prefill_full_size():
-    print("[case] linear la_prefill_b2_1024 sequential", flush=True)
-    w = wl.make_linear_config("la_prefill_b2_1024", device="cuda")
-    _check(w, "la_prefill_b2_1024-sequential", parallel=False)
+@pytest.mark.parametrize("name", ["la_prefill_b1_1024", "la_prefill_b2_1024"])
+def test_linear_named_prefills_chunked(name, path_env):
+    path_env("chunked")
+    print(f"[case] linear {name} chunked", flush=True)
+    w = wl.make_linear_config(name, device="cuda")
+    _check(w, name + "-chunked", "chunked")
 
 
 @needs_gpu
-def test_linear_parallel_prefill_long_request_with_state():
-    """A 3000-token request (47 chunks) next to short ones, from stored states."""
-    print("[case] linear prefill long request", flush=True)
+def test_linear_sequential_prefill_full_size():
+    print("[case] linear la_prefill_b2_1024 sequential", flush=True)
+    w = wl.make_linear_config("la_prefill_b2_1024", device="cuda")
+    _check(w, "la_prefill_b2_1024-sequential", "sequential")
+
+
+@needs_gpu
+@pytest.mark.parametrize("path", ["fused", "chunked"])
+def test_linear_parallel_prefill_long_request_with_state(path, path_env):
+    """A 3000-token request (47 chunks, 94 tiles) next to short ones, from stored states."""
+    path_env(path)
+    print(f"[case] linear prefill long request path={path}", flush=True)
     w = wl.make_linear(36, [3000, 5, 200], kind="prefill", initial_state=True, num_heads=2).to("cuda")
-    _check(w, "la-long")
+    _check(w, f"la-long-{path}", path)
+
+
+@needs_gpu
+def test_linear_prefill_past_the_closed_form_length():
+    """4200 tokens (above the closed form's 4096) next to a 4096-token request: the call takes the
+    chunk-parallel path."""
+    print("[case] linear prefill above 4096 tokens", flush=True)
+    w = wl.make_linear(38, [4200, 4096], kind="prefill", initial_state=True, num_heads=2).to("cuda")
+    _check(w, "la-4200", "chunked")
 
 
 @needs_gpu
@@ -153,10 +193,12 @@ def test_linear_decode_equals_one_token_prefill():
 
 
 @needs_gpu
-@pytest.mark.parametrize("parallel", [True, False], ids=["chunk-parallel", "sequential"])
-def test_linear_prefill_is_deterministic(parallel):
+@pytest.mark.parametrize("path", PATHS)
+def test_linear_prefill_is_deterministic(path, path_env):
     sa = _sa()
-    print(f"[case] linear prefill determinism parallel={parallel}", flush=True)
+    path_env(path)
+    parallel = path != "sequential"
+    print(f"[case] linear prefill determinism path={path}", flush=True)
     w = wl.make_linear(35, [300, 77], kind="prefill", num_heads=4).to("cuda")
     pool0 = w.state_pool.clone()
     o1 = sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool, parallel=parallel)
@@ -169,10 +211,12 @@ def test_linear_prefill_is_deterministic(parallel):
 
 
 @needs_gpu
-def test_linear_prefill_tokens_above_max_seqlen_give_nan():
-    """max_seqlen sizes the chunk-parallel workspace: tokens of a longer request past it and that
+@pytest.mark.parametrize("path", ["fused", "chunked"])
+def test_linear_prefill_tokens_above_max_seqlen_give_nan(path, path_env):
+    """max_seqlen bounds the request lengths: tokens of a longer request past it and that
     request's final state are NaN, the tokens before it are still correct."""
-    print("[case] linear prefill with a length above max_seqlen", flush=True)
+    path_env(path)
+    print(f"[case] linear prefill with a length above max_seqlen path={path}", flush=True)
     sa = _sa()
     w = wl.make_linear(37, [70, 40, 129], kind="prefill", initial_state=True, num_heads=4).to("cuda")
     pool_before = w.state_pool.detach().cpu().clone()
