@@ -106,6 +106,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base) {
 __device__ __forceinline__ void copy16_buf(__amdgpu_buffer_rsrc_t r, lds_void_t* lds_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
 }
+// The same with the non-temporal bit (data read once, in a stream), and 4 bytes per lane.
+__device__ __forceinline__ void copy16_buf_stream(__amdgpu_buffer_rsrc_t r, lds_void_t* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 2);
+}
+__device__ __forceinline__ void copy4_buf(__amdgpu_buffer_rsrc_t r, lds_void_t* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 4, voff, 0, 0, 0);
+}
 
 // Transposing LDS read: within each group of 16 lanes, lane i receives element (i % 4) of the
 // 4 bf16 values addressed by lane 4 * jj + i / 4, for jj = 0..3.

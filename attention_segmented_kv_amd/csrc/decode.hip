@@ -615,6 +615,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int grp = lane >> 4;  // 0..3
   const int hq = hkv * kGroup;
   const int64_t tok_bytes = (int64_t)hkv * C::kRowBytes;
+  // Byte offsets of this lane's copies within a tile whose rows are consecutive pool slots:
+  // copy i covers rows kRowsPerCopy * i .. + kRowsPerCopy - 1, lane piece lane % kChunks of row
+  // kRowsPerCopy * i + lane / kChunks (stored swizzled, so the piece read is chunk position ^ f(r))
+  uint32_t koff[C::kTile / C::kRowsPerCopy], voff[C::kTile / C::kRowsPerCopy];
+#pragma unroll
+  for (int i = 0; i < C::kTile / C::kRowsPerCopy; ++i) {
+    const int r = C::kRowsPerCopy * i + lane / C::kChunks;
+    const int cpos = lane % C::kChunks;
+    int kc, vc;
+    if constexpr (kKv == 0) {
+      kc = cpos ^ (r & 15);
+      vc = cpos ^ vswz16(r);
+    } else {
+      kc = cpos ^ (r & 7);
+      vc = kc;
+    }
+    koff[i] = (uint32_t)r * (uint32_t)tok_bytes + 16 * kc;
+    voff[i] = (uint32_t)r * (uint32_t)tok_bytes + 16 * vc;
+  }
+  const uint32_t soff = (uint32_t)lane * (uint32_t)hkv * 4;  // scale of row `lane`
 
   // Every field is wave-uniform and kept in scalar registers (readfirstlane after the integer
   // division, which the compiler does on the vector ALU); the chunk record is one scalar load.
@@ -693,59 +713,68 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const int last = min(m.k0 + C::kTile, m.kstop) - 1;
     cur.advance_to(m.k0);
     const bool fast = (m.k0 + C::kTile <= m.kstop) && (last - cur.start < cur.len);
-    const int rsub = lane / C::kChunks;
-    const int cpos = lane % C::kChunks;
     constexpr int kN = C::kTile / C::kRowsPerCopy;
-    // pool slot of each of this lane's kN rows
-    int64_t slot_of[kN];
+    const char* kbase = (const char*)k_pool + (int64_t)iu.g * C::kRowBytes;
+    const char* vbase = (const char*)v_pool + (int64_t)iu.g * C::kRowBytes;
     if (fast) {
+      // rows k0 .. k0 + kTile - 1 are consecutive pool slots from base: one buffer per tensor
+      // based at the tile's first row, and per-lane offsets fixed for the whole kernel
       const int64_t base = (int64_t)cur.off + (m.k0 - cur.start);
+      const auto kr = block_rsrc(kbase + base * tok_bytes);
+      const auto vr = block_rsrc(vbase + base * tok_bytes);
 #pragma unroll
-      for (int i = 0; i < kN; ++i) slot_of[i] = base + C::kRowsPerCopy * i + rsub;
+      for (int i = 0; i < kN; ++i) {
+        copy16_buf_stream(kr, (lds_void_t*)(kb + i * 1024), koff[i]);
+        copy16_buf_stream(vr, (lds_void_t*)(vb + i * 1024), voff[i]);
+      }
+      if constexpr (kKv != 0) {
+        // scales: lane L copies those of row L
+        const int64_t s0 = base * hkv + iu.g;
+        copy4_buf(block_rsrc(k_scale + s0), (lds_void_t*)(vb + C::kKBytes), soff);
+        copy4_buf(block_rsrc(v_scale + s0), (lds_void_t*)(vb + C::kKBytes + C::kScaleBytes), soff);
+      }
     } else {
       // Rows of the tile that straddle segments (or lie past the unit's end, which re-read
       // the unit's last key and are masked later): walk the overlapped segments with a
       // scalar copy of the cursor.
+      const int rsub = lane / C::kChunks;
+      const int cpos = lane % C::kChunks;
+      int64_t slot_of[kN];
 #pragma unroll
       for (int i = 0; i < kN; ++i) slot_of[i] = 0;
-      ScalarCursor c2 = cur;
-      while (true) {
+      {
+        ScalarCursor c2 = cur;
+        while (true) {
 #pragma unroll
-        for (int i = 0; i < kN; ++i) {
-          const int j = min(m.k0 + C::kRowsPerCopy * i + rsub, last);
-          if (j - c2.start >= 0 && j - c2.start < c2.len) slot_of[i] = (int64_t)c2.off + (j - c2.start);
+          for (int i = 0; i < kN; ++i) {
+            const int j = min(m.k0 + C::kRowsPerCopy * i + rsub, last);
+            if (j - c2.start >= 0 && j - c2.start < c2.len) slot_of[i] = (int64_t)c2.off + (j - c2.start);
+          }
+          if (last - c2.start < c2.len) break;
+          c2.start += c2.len;
+          ++c2.idx;
+          c2.fetch();
         }
-        if (last - c2.start < c2.len) break;
-        c2.start += c2.len;
-        ++c2.idx;
-        c2.fetch();
       }
-    }
-    const char* kbase = (const char*)k_pool + (int64_t)iu.g * C::kRowBytes;
-    const char* vbase = (const char*)v_pool + (int64_t)iu.g * C::kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int r = C::kRowsPerCopy * i + rsub;
-      int kc, vc;
-      if constexpr (kKv == 0) {
-        kc = cpos ^ (r & 15);
-        vc = cpos ^ vswz16(r);
-      } else {
-        kc = cpos ^ (r & 7);
-        vc = kc;
+      for (int i = 0; i < kN; ++i) {
+        const int r = C::kRowsPerCopy * i + rsub;
+        int kc, vc;
+        if constexpr (kKv == 0) {
+          kc = cpos ^ (r & 15);
+          vc = cpos ^ vswz16(r);
+        } else {
+          kc = cpos ^ (r & 7);
+          vc = kc;
+        }
+        const int64_t row = slot_of[i] * tok_bytes;
+        copy16_to_lds_stream(kbase + row + kc * 16, (lds_void_t*)(kb + i * 1024));
+        copy16_to_lds_stream(vbase + row + vc * 16, (lds_void_t*)(vb + i * 1024));
       }
-      const int64_t row = slot_of[i] * tok_bytes;
-      copy16_to_lds_stream(kbase + row + kc * 16, (lds_void_t*)(kb + i * 1024));
-      copy16_to_lds_stream(vbase + row + vc * 16, (lds_void_t*)(vb + i * 1024));
-    }
-    if constexpr (kKv != 0) {
-      // scales: lane L copies those of row L
-      const int j = min(m.k0 + lane, last);
-      int64_t s;
-      if (fast) {
-        s = (int64_t)cur.off + (j - cur.start);
-      } else {
-        s = 0;
+      if constexpr (kKv != 0) {
+        // scales: lane L copies those of row L
+        const int j = min(m.k0 + lane, last);
+        int64_t s = 0;
         ScalarCursor c2 = cur;
         while (true) {
           if (j - c2.start >= 0 && j - c2.start < c2.len) s = (int64_t)c2.off + (j - c2.start);
@@ -754,9 +783,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
           ++c2.idx;
           c2.fetch();
         }
+        copy4_to_lds(k_scale + s * hkv + iu.g, (lds_void_t*)(vb + C::kKBytes));
+        copy4_to_lds(v_scale + s * hkv + iu.g, (lds_void_t*)(vb + C::kKBytes + C::kScaleBytes));
       }
-      copy4_to_lds(k_scale + s * hkv + iu.g, (lds_void_t*)(vb + C::kKBytes));
-      copy4_to_lds(v_scale + s * hkv + iu.g, (lds_void_t*)(vb + C::kKBytes + C::kScaleBytes));
     }
     // advance to this wave's next tile
     it += kWaves;
