@@ -541,21 +541,37 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
   // the request's keys): row r of the block is pool slot base + r for the whole workgroup, a
   // scalar base plus a fixed per-thread offset. Otherwise every row is looked up on its own
   // (rows past K re-read key K - 1).
+  // Copies of block blk into (kdst, vdst). Fast case (the block inside one segment and inside
+  // the request's keys): row r of the block is pool slot base + r for the whole workgroup, a
+  // scalar base plus a fixed per-thread offset; its 8 copies are returned pending, to be issued
+  // one after each pair of MFMAs of the next S^T (copy_one). Otherwise every row is looked up on
+  // its own (rows past K re-read key K - 1) and the copies are issued at once.
+  struct Pending {
+    bool fast;
+    __amdgpu_buffer_rsrc_t kr, vr;
+    lds_char_t *lk, *lv;
+  };
+  auto copy_one = [&](const Pending& pc, int x) __attribute__((always_inline)) {
+    if (x < 4) copy16_buf(pc.kr, (lds_void_t*)(pc.lk + 1024 * x), koff[x]);
+    else copy16_buf(pc.vr, (lds_void_t*)(pc.lv + 1024 * (x - 4)), voff + (uint32_t)(16 * (x - 4)) * tok_bytes);
+  };
   auto issue_copies = [&](int blk, char* kdst, char* vdst) __attribute__((always_inline)) {
+    Pending pc;
     const int kb0 = blk * kBlockN;
     const int last = min(kb0 + kBlockN, K) - 1;
     cur.advance_to(kb0);
     lds_char_t* lk = (lds_char_t*)kdst + wave * 4096;
     lds_char_t* lv = (lds_char_t*)vdst + wave * 4096;
-    if ((kb0 + kBlockN <= K) && (last - cur.start < cur.len)) {
+    pc.lk = lk;
+    pc.lv = lv;
+    pc.fast = (kb0 + kBlockN <= K) && (last - cur.start < cur.len);
+    if (pc.fast) {
       const int64_t base = (int64_t)cur.off + (kb0 - cur.start);
-      const auto kr = block_rsrc(kbase + base * tok_stride);
-      const auto vr = block_rsrc(vbase + base * tok_stride);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) copy16_buf(kr, (lds_void_t*)(lk + 1024 * k), koff[k]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) copy16_buf(vr, (lds_void_t*)(lv + 1024 * k), voff + (uint32_t)(16 * k) * tok_bytes);
+      pc.kr = block_rsrc(kbase + base * tok_stride);
+      pc.vr = block_rsrc(vbase + base * tok_stride);
     } else {
+      pc.kr = block_rsrc(kbase);
+      pc.vr = pc.kr;
       SegCursor c2;
       c2.segs = cur.segs;
       c2.idx = cur.idx;
@@ -582,6 +598,7 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
         copy16_to_lds((const char*)(vbase + slot * tok_stride) + vcol, (lds_void_t*)(lv + 1024 * k));
       }
     }
+    return pc;
   };
 
   // LDS operand offsets (K swizzled row-major, V quarter-major; see the layouts at the top).
@@ -600,7 +617,7 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
 
   // One block: S^T = K Q^T, online softmax, O^T += V^T P^T. LDS operands are read ahead of the
   // MFMAs that use them (K two steps ahead, V one d tile ahead).
-  auto block_step = [&](int blk, const char* kslot, const char* vslot) __attribute__((always_inline)) {
+  auto block_step = [&](int blk, const char* kslot, const char* vslot, const Pending& pc, bool more) __attribute__((always_inline)) {
     const lds_char_t* kb = (const lds_char_t*)kslot;
     const lds_char_t* vb = (const lds_char_t*)vslot;
     f32x16 s0, s1;
@@ -619,6 +636,7 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
         }
         s0 = mfma32x32x16(ka[step % 3][0], qf[step], step == 0 ? f32x16{} : s0);
         s1 = mfma32x32x16(ka[step % 3][1], qf[step], step == 0 ? f32x16{} : s1);
+        if (more && pc.fast) copy_one(pc, step);
         if (step + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -731,17 +749,24 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
   // Block j runs from slot j & 1; the copies of block j + 1 go to the other slot, which every
   // wave finished reading before the barrier that ended the step before.
   if (nblk > 0) {
-    issue_copies(0, lk0, lv0);
+    {
+      const Pending p0 = issue_copies(0, lk0, lv0);
+      if (p0.fast)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) copy_one(p0, x);
+    }
     wait_vmem();  // also the Q loads
     phase_barrier();
     for (int j = 0; j < nblk; j += 2) {
-      if (j + 1 < nblk) issue_copies(j + 1, lk1, lv1);
-      block_step(j, lk0, lv0);
+      const bool more1 = j + 1 < nblk;
+      Pending pc = more1 ? issue_copies(j + 1, lk1, lv1) : Pending{};
+      block_step(j, lk0, lv0, pc, more1);
       wait_vmem();
       phase_barrier();
-      if (j + 1 >= nblk) break;
-      if (j + 2 < nblk) issue_copies(j + 2, lk0, lv0);
-      block_step(j + 1, lk1, lv1);
+      if (!more1) break;
+      const bool more2 = j + 2 < nblk;
+      pc = more2 ? issue_copies(j + 2, lk0, lv0) : Pending{};
+      block_step(j + 1, lk1, lv1, pc, more2);
       wait_vmem();
       phase_barrier();
     }
