@@ -34,8 +34,16 @@ _KV_OF_DTYPE = {torch.bfloat16: KV_BF16, torch.float8_e4m3fn: KV_FP8_E4M3, torch
 HEAD_DIM = 128
 GROUP = 8
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsegattn.so")
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_FILES = {"release": "libsegattn.so", "debug": "libsegattn_debug.so"}
+# SEG_ATTN_LIBRARY=debug makes the binding load the debug build (tables checked on the host
+# before every attention launch; see seg_attn_debug_build in include/seg_attn.h)
+_VARIANT = os.environ.get("SEG_ATTN_LIBRARY", "release")
+if _VARIANT not in _LIB_FILES:
+    raise ValueError(f"SEG_ATTN_LIBRARY must be one of {sorted(_LIB_FILES)}, not {_VARIANT!r}")
+_LIB_PATH = os.path.join(_PKG_DIR, _LIB_FILES[_VARIANT])
 _lib = None
+_libs = {}
 
 
 class SegAttnError(RuntimeError):
@@ -44,18 +52,27 @@ class SegAttnError(RuntimeError):
         self.status = status
 
 
-def library_path() -> str:
-    return _LIB_PATH
+def library_path(variant: Optional[str] = None) -> str:
+    """Path of the library the binding loads, or of the named variant ("release", "debug")."""
+    return _LIB_PATH if variant is None else os.path.join(_PKG_DIR, _LIB_FILES[variant])
 
 
 def _load():
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
-                           "`python -m attention_segmented_kv_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _lib is None:
+        _lib = load_library(_VARIANT)
+    return _lib
+
+
+def load_library(variant: str = "release"):
+    """The ctypes handle of a library variant, with every entry point's signature set."""
+    if variant in _libs:
+        return _libs[variant]
+    path = library_path(variant)
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m attention_segmented_kv_amd.build --all` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
     P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.seg_attn_prefill.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I64, F32, I32, P, P, P]
     lib.seg_attn_prefill.restype = I32
@@ -113,7 +130,9 @@ def _load():
     lib.seg_attn_allocator_compact.restype = I32
     lib.seg_attn_kv_move.argtypes = [P, I32, I64, I32, I32, I64, I32, P, P, P, P, P]
     lib.seg_attn_kv_move.restype = I32
-    _lib = lib
+    lib.seg_attn_debug_build.argtypes = []
+    lib.seg_attn_debug_build.restype = I32
+    _libs[variant] = lib
     return lib
 
 

@@ -1,6 +1,6 @@
 """Build libsegattn.so for gfx950 in-tree with hipcc.
 
-Usage: python -m attention_segmented_kv_amd.build [--verbose]
+Usage: python -m attention_segmented_kv_amd.build [--verbose] [--debug | --all]
 """
 from __future__ import annotations
 
@@ -14,7 +14,6 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
-LIB = os.path.join(PKG, "libsegattn.so")
 SOURCES = ["api.hip", "prefill.hip", "decode.hip", "append.hip", "linear.hip", "allocator.cpp"]
 ARCH = "gfx950"
 
@@ -42,23 +41,46 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source for gfx950 and link libsegattn.so next to this file."""
-    os.makedirs(BUILD, exist_ok=True)
+# Variants: "release" (libsegattn.so) and "debug" (libsegattn_debug.so: SEG_ATTN_DEBUG, whose
+# entry points check the segment tables on the host before every attention launch).
+VARIANTS = {
+    "release": ("libsegattn.so", []),
+    "debug": ("libsegattn_debug.so", ["-DSEG_ATTN_DEBUG=1", "-g"]),
+}
+
+
+def library_file(variant: str = "release") -> str:
+    return os.path.join(PKG, VARIANTS[variant][0])
+
+
+def build(verbose: bool = False, extra_flags=(), variant: str = "release") -> str:
+    """Compile every HIP source for gfx950 and link the variant's library next to this file."""
+    name, vflags = VARIANTS[variant]
+    bdir = os.path.join(BUILD, variant)
+    os.makedirs(bdir, exist_ok=True)
     cc = hipcc()
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *HIP_FLAGS, *vflags, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    lib = os.path.join(PKG, name)
+    tmp = lib + ".tmp"
     _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build_all(verbose: bool = False):
+    """Both variants."""
+    return [build(verbose, variant=v) for v in VARIANTS]
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    if "--all" in sys.argv:
+        print("\n".join(build_all(verbose="--verbose" in sys.argv)))
+    else:
+        print(build(verbose="--verbose" in sys.argv, variant="debug" if "--debug" in sys.argv else "release"))

@@ -10,6 +10,12 @@
 
 #include "../../include/seg_attn.h"
 
+#ifdef SEG_ATTN_DEBUG
+constexpr bool kDebugBuild = true;
+#else
+constexpr bool kDebugBuild = false;
+#endif
+
 namespace segattn {
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool, const void* segs,
                           const int32_t* seg_indptr, const int32_t* cu_q, const int32_t* cu_k,
@@ -148,6 +154,84 @@ seg_attn_status_t check_heads(int32_t hq, int32_t hkv, int32_t head_dim) {
   return SEG_ATTN_OK;
 }
 
+seg_attn_status_t check_tables(const seg_attn_segment_t* segs, int64_t nseg,
+                                           const int32_t* seg_indptr,
+                                           const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_k, int32_t batch,
+                                           int64_t pool_tokens, int32_t causal,
+                                           int64_t* bad_index, bool disjoint) {
+  try {
+    auto fail = [&](int64_t i) {
+      if (bad_index) *bad_index = i;
+      return (seg_attn_status_t)SEG_ATTN_ERR_TABLE;
+    };
+    if (batch < 0 || nseg < 0 || pool_tokens < 0) return SEG_ATTN_ERR_INVALID_ARG;
+    if (!seg_indptr || !cu_seqlens_k || (nseg > 0 && !segs)) return SEG_ATTN_ERR_INVALID_ARG;
+    if (seg_indptr[0] != 0 || cu_seqlens_k[0] != 0) return fail(0);
+    if (cu_seqlens_q && cu_seqlens_q[0] != 0) return fail(0);
+    if (seg_indptr[batch] != nseg) return fail(batch);
+    for (int32_t b = 0; b < batch; ++b) {
+      if (seg_indptr[b + 1] < seg_indptr[b]) return fail(b);
+      const int64_t kb = (int64_t)cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+      if (kb < 0) return fail(b);
+      const int64_t lq = cu_seqlens_q ? (int64_t)cu_seqlens_q[b + 1] - cu_seqlens_q[b] : 1;
+      if (lq < 0) return fail(b);
+      if (causal && lq > kb) return fail(b);
+      int64_t sum = 0;
+      for (int32_t s = seg_indptr[b]; s < seg_indptr[b + 1]; ++s) {
+        if (segs[s].length < 0 || segs[s].pool_offset < 0 ||
+            (int64_t)segs[s].pool_offset + segs[s].length > pool_tokens)
+          return fail(s);
+        sum += segs[s].length;
+      }
+      if (sum != kb) return fail(b);
+    }
+    // no two non-empty segments may share a pool slot
+    if (!disjoint) {
+      if (bad_index) *bad_index = -1;
+      return SEG_ATTN_OK;
+    }
+    std::vector<std::pair<int64_t, int64_t>> iv;  // (start, segment index)
+    iv.reserve((size_t)nseg);
+    for (int64_t s = 0; s < nseg; ++s)
+      if (segs[s].length > 0) iv.emplace_back(segs[s].pool_offset, s);
+    std::sort(iv.begin(), iv.end());
+    for (size_t i = 1; i < iv.size(); ++i) {
+      const auto& prev = segs[iv[i - 1].second];
+      if ((int64_t)prev.pool_offset + prev.length > iv[i].first) return fail(iv[i].second);
+    }
+    if (bad_index) *bad_index = -1;
+    return SEG_ATTN_OK;
+  } catch (...) {
+    return SEG_ATTN_ERR_HIP;
+  }
+}
+
+// Debug builds (SEG_ATTN_DEBUG) check the device tables on the host before every attention
+// launch: the stream is synchronised, the tables are copied back and checked as
+// seg_attn_validate_tables does, except that segments of different requests may share slots
+// (attention only reads them); a call on broken tables returns SEG_ATTN_ERR_TABLE and launches
+// nothing, so every pool slot a kernel resolves lies inside [0, pool_tokens).
+seg_attn_status_t debug_check_tables(const seg_attn_segment_t* segs, const int32_t* seg_indptr,
+                                     const int32_t* cu_q, const int32_t* cu_k, int32_t batch,
+                                     int64_t pool_tokens, int32_t causal, hipStream_t stream) {
+  if (!kDebugBuild) return SEG_ATTN_OK;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SEG_ATTN_ERR_HIP;
+  const size_t nb = (size_t)batch + 1;
+  std::vector<int32_t> ind(nb), ck(nb), cq(cu_q ? nb : 0);
+  if (hipMemcpy(ind.data(), seg_indptr, nb * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(ck.data(), cu_k, nb * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      (cu_q && hipMemcpy(cq.data(), cu_q, nb * 4, hipMemcpyDeviceToHost) != hipSuccess))
+    return SEG_ATTN_ERR_HIP;
+  const int64_t nseg = ind[batch];
+  if (nseg < 0 || nseg > (int64_t)1 << 30) return SEG_ATTN_ERR_TABLE;
+  std::vector<seg_attn_segment_t> sg((size_t)nseg);
+  if (nseg > 0 && hipMemcpy(sg.data(), segs, (size_t)nseg * sizeof(seg_attn_segment_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return SEG_ATTN_ERR_HIP;
+  return check_tables(sg.data(), nseg, ind.data(), cu_q ? cq.data() : nullptr, ck.data(), batch, pool_tokens,
+                      causal, nullptr, false);
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,6 +249,8 @@ const char* seg_attn_status_string(seg_attn_status_t status) {
     default: return "unknown status";
   }
 }
+
+int32_t seg_attn_debug_build(void) { return kDebugBuild ? 1 : 0; }
 
 int32_t seg_attn_version(void) { return 1 * 10000 + 0 * 100 + 0; }
 
@@ -194,6 +280,9 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
       return SEG_ATTN_ERR_INVALID_ARG;
     const int64_t grid = ceil_div(max_seqlen_q, 16) * (int64_t)num_heads_kv * batch;
     if (grid > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;
+    const seg_attn_status_t ts = debug_check_tables(segs, seg_indptr, cu_seqlens_q, cu_seqlens_k, batch,
+                                                    pool_tokens, causal, (hipStream_t)stream);
+    if (ts != SEG_ATTN_OK) return ts;
     hipError_t e = segattn::launch_prefill(q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_q,
                                            cu_seqlens_k, batch, max_seqlen_q, num_heads_kv,
                                            softmax_scale, causal, out, lse, current_cu_count(),
@@ -293,6 +382,11 @@ seg_attn_status_t decode_impl(const void* q, const void* k_pool, const void* v_p
     return SEG_ATTN_ERR_INVALID_ARG;
   DecodePlan p;
   if (!plan_decode(batch, max_seqlen_k, scaled, num_splits, &p)) return SEG_ATTN_ERR_INVALID_ARG;
+  {
+    const seg_attn_status_t ts = debug_check_tables(segs, seg_indptr, nullptr, cu_seqlens_k, batch, pool_tokens,
+                                                    0, stream);
+    if (ts != SEG_ATTN_OK) return ts;
+  }
   int64_t max_chunks = p.per_request * batch;
   int cu_count = 0;  // read from the device only once the call is going to launch
   if (noalloc && num_splits == 0) {
@@ -506,47 +600,8 @@ seg_attn_status_t seg_attn_validate_tables(const seg_attn_segment_t* segs, int64
                                            const int32_t* cu_seqlens_k, int32_t batch,
                                            int64_t pool_tokens, int32_t causal,
                                            int64_t* bad_index) {
-  try {
-    auto fail = [&](int64_t i) {
-      if (bad_index) *bad_index = i;
-      return (seg_attn_status_t)SEG_ATTN_ERR_TABLE;
-    };
-    if (batch < 0 || nseg < 0 || pool_tokens < 0) return SEG_ATTN_ERR_INVALID_ARG;
-    if (!seg_indptr || !cu_seqlens_k || (nseg > 0 && !segs)) return SEG_ATTN_ERR_INVALID_ARG;
-    if (seg_indptr[0] != 0 || cu_seqlens_k[0] != 0) return fail(0);
-    if (cu_seqlens_q && cu_seqlens_q[0] != 0) return fail(0);
-    if (seg_indptr[batch] != nseg) return fail(batch);
-    for (int32_t b = 0; b < batch; ++b) {
-      if (seg_indptr[b + 1] < seg_indptr[b]) return fail(b);
-      const int64_t kb = (int64_t)cu_seqlens_k[b + 1] - cu_seqlens_k[b];
-      if (kb < 0) return fail(b);
-      const int64_t lq = cu_seqlens_q ? (int64_t)cu_seqlens_q[b + 1] - cu_seqlens_q[b] : 1;
-      if (lq < 0) return fail(b);
-      if (causal && lq > kb) return fail(b);
-      int64_t sum = 0;
-      for (int32_t s = seg_indptr[b]; s < seg_indptr[b + 1]; ++s) {
-        if (segs[s].length < 0 || segs[s].pool_offset < 0 ||
-            (int64_t)segs[s].pool_offset + segs[s].length > pool_tokens)
-          return fail(s);
-        sum += segs[s].length;
-      }
-      if (sum != kb) return fail(b);
-    }
-    // no two non-empty segments may share a pool slot
-    std::vector<std::pair<int64_t, int64_t>> iv;  // (start, segment index)
-    iv.reserve((size_t)nseg);
-    for (int64_t s = 0; s < nseg; ++s)
-      if (segs[s].length > 0) iv.emplace_back(segs[s].pool_offset, s);
-    std::sort(iv.begin(), iv.end());
-    for (size_t i = 1; i < iv.size(); ++i) {
-      const auto& prev = segs[iv[i - 1].second];
-      if ((int64_t)prev.pool_offset + prev.length > iv[i].first) return fail(iv[i].second);
-    }
-    if (bad_index) *bad_index = -1;
-    return SEG_ATTN_OK;
-  } catch (...) {
-    return SEG_ATTN_ERR_HIP;
-  }
+  return check_tables(segs, nseg, seg_indptr, cu_seqlens_q, cu_seqlens_k, batch, pool_tokens, causal,
+                      bad_index, true);
 }
 
 }  // extern "C"

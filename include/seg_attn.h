@@ -70,7 +70,7 @@ enum {
   SEG_ATTN_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim != 128 or Hq/Hkv != 8 */
   SEG_ATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
   SEG_ATTN_ERR_HIP = 4,         /* the HIP runtime reported an error at launch */
-  SEG_ATTN_ERR_TABLE = 5,       /* seg_attn_validate_tables found an inconsistent table */
+  SEG_ATTN_ERR_TABLE = 5,       /* inconsistent tables (seg_attn_validate_tables, debug builds) */
   SEG_ATTN_ERR_OUT_OF_MEMORY = 6, /* the allocator's pool (or the host heap) cannot hold it */
   SEG_ATTN_ERR_SCRATCH = 7        /* seg_attn_decode_noalloc: more than its fixed scratch holds */
 };
@@ -421,6 +421,17 @@ seg_attn_status_t seg_attn_validate_tables(const seg_attn_segment_t* segs, int64
 
 /* Library version as major * 10000 + minor * 100 + patch. */
 int32_t seg_attn_version(void);
+
+/*
+ * 1 for the library built with SEG_ATTN_DEBUG (libsegattn_debug.so, for tests and bring-up),
+ * 0 for the release library. The debug build synchronises the stream before every attention
+ * call (prefill and decode, including the entry point that allocates nothing), copies the segment
+ * tables back to the host and checks them as seg_attn_validate_tables does, except that segments
+ * of different requests may share slots (attention only reads them). Broken tables make the call
+ * return SEG_ATTN_ERR_TABLE with nothing launched, so no kernel resolves a pool slot outside
+ * [0, pool_tokens). The check costs a host round trip per call.
+ */
+int32_t seg_attn_debug_build(void);
 
 #ifdef __cplusplus
 }

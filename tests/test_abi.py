@@ -38,6 +38,23 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(sa.library_path())
     for s in declared_symbols():
         assert hasattr(raw, s), f"{s} not exported"
+
+
+@pytest.mark.parametrize("variant,flag", [("release", 0), ("debug", 1)])
+def test_both_library_variants_load_and_say_which_they_are(variant, flag):
+    """The release and the debug (SEG_ATTN_DEBUG) libraries both export the whole header and
+    report their variant; they share every argument check."""
+    if not os.path.exists(sa.library_path(variant)):
+        pytest.skip(f"{variant} library not built")
+    lib = sa.load_library(variant)
+    raw = ctypes.CDLL(sa.library_path(variant))
+    for s in declared_symbols():
+        assert hasattr(raw, s), f"{s} not exported by the {variant} library"
+    assert lib.seg_attn_debug_build() == flag
+    assert lib.seg_attn_version() == sa.load_library("release").seg_attn_version()
+    # an argument error is still caught before anything else (no table read, no launch)
+    P = None
+    assert lib.seg_attn_prefill(P, P, P, P, P, P, P, 1, 8, 8, 64, 8, 128, 100, 0.1, 1, P, P, P) == 1
     assert lib.seg_attn_version() == 10000
 
 
