@@ -560,8 +560,9 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
     const int kb0 = blk * kBlockN;
     const int last = min(kb0 + kBlockN, K) - 1;
     cur.advance_to(kb0);
-    lds_char_t* lk = (lds_char_t*)kdst + wave * 4096;
-    lds_char_t* lv = (lds_char_t*)vdst + wave * 4096;
+    // the wave's LDS destinations as scalars: every copy's M0 is then a scalar add
+    lds_char_t* lk = (lds_char_t*)(uintptr_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)((lds_char_t*)kdst + wave * 4096));
+    lds_char_t* lv = (lds_char_t*)(uintptr_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)((lds_char_t*)vdst + wave * 4096));
     pc.lk = lk;
     pc.lv = lv;
     pc.fast = (kb0 + kBlockN <= K) && (last - cur.start < cur.len);
