@@ -29,6 +29,8 @@
 // attention over the dequantised pool with the probabilities rounded to bf16 (f16 for INT8).
 //
 // Merge pass: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s per (request, head).
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "common.hpp"
@@ -313,9 +315,11 @@ constexpr int kBuckets = 256;
 constexpr int kPlanSegs = 8;  // segments per request read up front
 constexpr int kSpreadMax = 512;  // plan: batches up to this size share each request's chunks
 
-// Inclusive scan over the 1024 threads of the block of two counts at once: shuffles within each
-// wave, then one pass over the 16 wave totals. wtot is LDS scratch of 2 x 16 ints.
+// Inclusive scan over the kW waves of the block of two counts at once: shuffles within each
+// wave, then one pass over the wave totals. wtot is LDS scratch of 2 x 16 ints.
+template <int kW>
 __device__ __forceinline__ void block_scan2(int& a, int& b, int* wtot) {
+  static_assert(kW >= 1 && kW <= 16, "at most 16 waves");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -331,7 +335,7 @@ __device__ __forceinline__ void block_scan2(int& a, int& b, int* wtot) {
   }
   __syncthreads();
   if (w == 0) {
-    int x = lane < 16 ? wtot[lane] : 0, y = lane < 16 ? wtot[16 + lane] : 0;
+    int x = lane < kW ? wtot[lane] : 0, y = lane < kW ? wtot[16 + lane] : 0;
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) {
       const int tx = __shfl_up(x, d), ty = __shfl_up(y, d);
@@ -340,7 +344,7 @@ __device__ __forceinline__ void block_scan2(int& a, int& b, int* wtot) {
         y += ty;
       }
     }
-    if (lane < 16) {
+    if (lane < kW) {
       wtot[lane] = x;
       wtot[16 + lane] = y;
     }
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
     counts(K, n, f);
     if (n > f) atomicAdd(&hist[(int)((int64_t)(K - f * len) * kBuckets / len)], 1);
     int sn = n, sf = f;
-    block_scan2(sn, sf, wtot);
+    block_scan2<16>(sn, sf, wtot);
     if (b0 == 0) {
       sn0 = sn;
       sf0 = sf;
@@ -439,7 +443,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
   // bucket positions, longest short chunks first: a scan over the buckets in reverse order
   {
     int hcount = tid < kBuckets ? hist[kBuckets - 1 - tid] : 0, dummy = 0;
-    block_scan2(hcount, dummy, wtot);
+    block_scan2<16>(hcount, dummy, wtot);
     if (tid < kBuckets) bucket_base[kBuckets - 1 - tid] = total_f + hcount - hist[kBuckets - 1 - tid];
   }
   __syncthreads();
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
       counts(K, n, f);
       sn = n;
       sf = f;
-      block_scan2(sn, sf, wtot);
+      block_scan2<16>(sn, sf, wtot);
     }
     const int first = cn + sn - n;   // first chunk index of request b
     const int ffirst = cf + sf - f;  // schedule position of its first full chunk
@@ -572,14 +576,173 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
+// The plan inside the split pass, for batches of at most kInPlanBatch requests with the automatic
+// chunk length: every workgroup derives the chunk list from the key counts itself, so the call
+// needs no separate plan launch (whose few microseconds, plus the gap before the next launch, are
+// a visible share of a short decode). The chunking (length, per-request chunk indices, hence
+// every partial and the merge order) is the plan kernel's; the schedule differs only in how the
+// short last chunks are ordered: by exact decreasing length, equal lengths by request, a total
+// order that every workgroup computes alike.
+constexpr int kInPlanBatch = kDecThreads;  // one request per thread
+constexpr int kUnitCap = 24;               // unit records per workgroup
+// Units per workgroup the automatic chunk length aims at. Measured over 4, 6, 8, 12 and 16 on
+// the bf16 batch-128 and the FP8 / INT8 batch-16 long-context decodes: 6 was the fastest or
+// within 1% of it on each; 4 leaves the longest requests' chunks too long to balance, 12 and
+// more pay for the extra partial results and merge work.
+constexpr int kUnitsPerWorkgroup = 6;
+
+// Units of schedule column p out of n_chunks over P columns (positions r * P + p for even r and
+// r * P + P - 1 - p for odd r).
+__device__ __forceinline__ int column_units(int n_chunks, int P, int p) {
+  const int full_rounds = n_chunks / P;
+  const int last_pos = (full_rounds & 1) ? P - 1 - p : p;
+  return full_rounds + (last_pos < n_chunks - full_rounds * P ? 1 : 0);
+}
+
+// All threads of the workgroup call this. scr: LDS for 6 x 257 + 40 ints that no copy writes
+// until it returns; utab: kUnitCap records of 3 x i32x4, laid out as the plan kernel's records.
+// Returns the chunk count, or -1 when some K_b exceeds max_k, the chunks would not fit in the
+// workspace (max_chunks) or a column would hold more than kUnitCap units; workgroup 0 then
+// writes hdr so that the merge pass marks every output NaN. Workgroup 0 also writes hdr and
+// chunk_base for the merge pass in the good case.
+__device__ int plan_in_workgroup(const int32_t* __restrict__ cu_k, const int32_t* __restrict__ seg_indptr,
+                                 const Segment* __restrict__ segs, int batch, int hkv, int min_len,
+                                 int target_units, int max_chunks, int max_k, int P, int p, int* scr,
+                                 i32x4* utab, int32_t* __restrict__ hdr, int32_t* __restrict__ chunk_base) {
+  int* sK = scr;             // [256] key count of each request
+  int* sF = sK + 256;        // [257] schedule position of each request's first full chunk
+  int* sN = sF + 257;        // [257] index of each request's first chunk
+  int* sA = sN + 257;        // [257] segment index range starts (seg_indptr)
+  int* sS = sA + 257;        // [256] length of the request's short last chunk, -1 if none
+  int* sO = sS + 256;        // [256] requests with a short chunk, longest chunk first
+  int* sW = sO + 256;        // [32] scan scratch
+  const int t = threadIdx.x;
+  const int64_t total = (int64_t)cu_k[batch] - cu_k[0];
+  int K = 0, sa = 0, sa_end = 0;
+  if (t < batch) {
+    K = cu_k[t + 1] - cu_k[t];
+    sa = seg_indptr[t];
+    if (t == batch - 1) sa_end = seg_indptr[batch];
+  }
+  int64_t want = (total * hkv + target_units - 1) / target_units;
+  want = (want + 63) / 64 * 64;
+  const int len = (int)(want < min_len ? min_len : (want > (1 << 30) ? (1 << 30) : want));
+  const int n = K > 0 ? (K + len - 1) / len : 0;
+  const int f = K > 0 ? K / len : 0;
+  int sn = n, sf = f;
+  block_scan2<kDecThreads / 64>(sn, sf, sW);
+  if (t < batch) {
+    sK[t] = K;
+    sF[t] = sf - f;
+    sN[t] = sn - n;
+    sA[t] = sa;
+    sS[t] = n > f ? K - f * len : -1;
+  }
+  if (t == batch - 1) {
+    sF[batch] = sf;
+    sN[batch] = sn;
+    sA[batch] = sa_end;
+  }
+  const int any_long = __syncthreads_or(t < batch && K > max_k);
+  const int total_f = sF[batch], total_n = sN[batch];
+  const bool bad = any_long != 0 || total_n > max_chunks || (total_n + P - 1) / P > kUnitCap;
+  if (blockIdx.x == 0) {
+    if (t == 0) {
+      hdr[0] = len;
+      hdr[1] = bad ? 0 : total_n;
+      hdr[2] = bad ? 1 : 0;
+      chunk_base[batch] = total_n;
+    }
+    if (t < batch) chunk_base[t] = sN[t];
+  }
+  if (bad) return -1;
+  // rank of each short chunk: longer ones first, equal lengths in request order
+  if (t < batch && n > f) {
+    const int sl = K - f * len;
+    int r = 0;
+    for (int u = 0; u < batch; ++u) {
+      const int su = sS[u];
+      r += (su > sl || (su == sl && u < t)) ? 1 : 0;
+    }
+    sO[r] = t;
+  }
+  __syncthreads();
+  // records of this column's units, one thread each
+  const int my_units = column_units(total_n, P, p);
+  if (t < my_units) {
+    const int r = t;
+    const int pos = r * P + ((r & 1) ? P - 1 - p : p);
+    int b, k;
+    if (pos < total_f) {
+      // the last request whose first full chunk is at or before pos owns it
+      int lo = 0, hi = batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sF[mid] <= pos) lo = mid;
+        else hi = mid - 1;
+      }
+      b = lo;
+      k = pos - sF[b];
+    } else {
+      b = sO[pos - total_f];
+      k = sK[b] / len;
+    }
+    const int Kb = sK[b];
+    const int kbeg = k * len;
+    const int kstop = min(Kb, kbeg + len);
+    const int single = (Kb + len - 1) / len == 1 ? 1 : 0;
+    const int c = sN[b] + k;
+    // the segment holding key kbeg: the request's segments in key order, 8 reads at a time
+    const int s_first = sA[b], s_end = sA[b + 1];
+    int idx = s_first, start = 0, sidx = s_end, soff = 0, slen = 0x7fffffff;
+    bool found = false;
+    while (!found && idx < s_end) {
+      const int m = min(8, s_end - idx);
+      Segment sg[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sg[j] = segs[idx + min(j, m - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (!found && j < m) {
+          if (kbeg - start < sg[j].length) {
+            found = true;
+            sidx = idx + j;
+            soff = sg[j].pool_offset;
+            slen = sg[j].length;
+          } else {
+            start += sg[j].length;
+          }
+        }
+      }
+      idx += m;
+    }
+    utab[3 * r + 0] = i32x4{b, kbeg, kstop, single};
+    utab[3 * r + 1] = i32x4{sidx, s_end, start, soff};
+    utab[3 * r + 2] = i32x4{slen, c, 0, 0};
+  }
+  __syncthreads();
+  return total_n;
+}
+
+// ------------------------------------------------------------------------------------------
 // Split pass.
-template <int kKv>
+// kInPlan: the workgroup plans for itself (plan_in_workgroup, from cu_k and seg_indptr, and
+// writes hdr and chunk_base for the merge pass); otherwise hdr and recs come from the plan kernel.
+struct InPlanArgs {
+  const int32_t* cu_k;
+  const int32_t* seg_indptr;
+  int32_t* chunk_base;
+  int batch, min_len, target_units, max_chunks, max_k;
+};
+
+template <int kKv, bool kInPlan>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const bf16_t* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-    const Segment* __restrict__ segs, const int32_t* __restrict__ hdr,
-    const int32_t* __restrict__ recs, int hkv, float scale, float scale_log2, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, bf16_t* __restrict__ out, float* __restrict__ lse) {
+    const Segment* __restrict__ segs, int32_t* __restrict__ hdr,
+    const int32_t* __restrict__ recs, InPlanArgs ipa, int hkv, float scale, float scale_log2,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, bf16_t* __restrict__ out,
+    float* __restrict__ lse) {
   using C = DecodeCfg<kKv>;
   using L = DecodeLayout<kKv>;
   // Separate objects for the two stages, the combine area and the Q tiles: the compiler then
@@ -590,8 +753,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   __shared__ __attribute__((aligned(16))) float comb[kWaves * L::kCombFloats];
   __shared__ __attribute__((aligned(16))) char qbuf[kQBufs * kQBytes];
   __shared__ __attribute__((aligned(16))) i32x4 uring[4];
+  __shared__ __attribute__((aligned(16))) i32x4 utab[kInPlan ? 3 * kUnitCap : 1];
 
-  const int n_chunks = rfl(hdr[1]);
   // Workgroup = (column p, lane g of the kv heads). Column p takes schedule positions r * P + p
   // for even r and r * P + P - 1 - p for odd r; in round r its workgroups take kv heads
   // (g + r) % hkv, so the 8 heads of each chunk are all done and every workgroup meets every
@@ -603,9 +766,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int P = gridDim.x / hkv;
   const int g = rfl(blockIdx.x / P);
   const int p = rfl(blockIdx.x - g * P);
-  const int full_rounds = n_chunks / P;
-  const int last_pos = (full_rounds & 1) ? P - 1 - p : p;
-  const int my_units = full_rounds + (last_pos < n_chunks - full_rounds * P ? 1 : 0);
+  int n_chunks;
+  if constexpr (kInPlan) {
+    // the per-request values go to stage 1, which no copy fills before this returns
+    n_chunks = plan_in_workgroup(ipa.cu_k, ipa.seg_indptr, segs, ipa.batch, hkv, ipa.min_len,
+                                 ipa.target_units, ipa.max_chunks, ipa.max_k, P, p,
+                                 reinterpret_cast<int*>(st1), utab, hdr, ipa.chunk_base);
+    if (n_chunks < 0) return;
+    n_chunks = rfl(n_chunks);
+  } else {
+    n_chunks = rfl(hdr[1]);
+  }
+  const int my_units = column_units(n_chunks, P, p);
   if (my_units == 0) return;
 
   const int tid = threadIdx.x;
@@ -641,9 +813,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   auto unit_info = [&](int r) __attribute__((always_inline)) {
     UnitInfo u;
     u.valid = r < my_units;
-    const int pos = u.valid ? r * P + ((r & 1) ? P - 1 - p : p) : 0;
-    const i32x4* rp = reinterpret_cast<const i32x4*>(recs + (int64_t)pos * kRecInts);
-    const i32x4 r0 = rp[0], r1 = rp[1], r2 = rp[2];
+    i32x4 r0, r1, r2;
+    if constexpr (kInPlan) {
+      // from the LDS table (through inline asm, so that the compiler adds no wait for the copies
+      // in flight)
+      const uint32_t a = (uint32_t)(uintptr_t)((lds_char_t*)utab + 48 * (u.valid ? r : 0));
+      asm volatile(
+          "ds_read_b128 %0, %3\n\t"
+          "ds_read_b128 %1, %3 offset:16\n\t"
+          "ds_read_b128 %2, %3 offset:32\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(r0), "=&v"(r1), "=&v"(r2)
+          : "v"(a)
+          : "memory");
+    } else {
+      const int pos = u.valid ? r * P + ((r & 1) ? P - 1 - p : p) : 0;
+      const i32x4* rp = reinterpret_cast<const i32x4*>(recs + (int64_t)pos * kRecInts);
+      r0 = rp[0];
+      r1 = rp[1];
+      r2 = rp[2];
+    }
     u.g = (g + r) % hkv;
     u.b = rfl(r0[0]);
     u.kbeg = rfl(r0[1]);
@@ -1115,11 +1304,6 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws
 
 }  // namespace
 
-// Units per workgroup the automatic chunk length aims at. Measured over 4, 6, 8, 12 and 16 on
-// the bf16 batch-128 and the FP8 / INT8 batch-16 long-context decodes: 6 was the fastest or
-// within 1% of it on each; 4 leaves the longest requests' chunks too long to balance, 12 and
-// more pay for the extra partial results and merge work.
-constexpr int kUnitsPerWorkgroup = 6;
 
 // An upper bound of the chunks the automatic plan lists (num_splits = 0), whatever the key
 // counts: the length it picks is at least total * hkv / target, target = kUnitsPerWorkgroup *
@@ -1129,6 +1313,13 @@ constexpr int kUnitsPerWorkgroup = 6;
 int64_t decode_auto_chunk_bound(int64_t batch, int hkv, int cu_count) {
   const int64_t cols = std::max(1, cu_count / std::max(1, hkv));
   return kUnitsPerWorkgroup * cols + 2 * batch;
+}
+
+// SEG_ATTN_DECODE_PLAN=kernel keeps the separate plan launch for every call (tests compare the
+// two ways of planning).
+bool decode_plan_kernel_forced() {
+  const char* v = std::getenv("SEG_ATTN_DECODE_PLAN");
+  return v != nullptr && std::strcmp(v, "kernel") == 0;
 }
 
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -1142,16 +1333,28 @@ hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
   const int cols = (int)std::max<int64_t>(1, std::min<int64_t>(cu_count / hkv, max_chunks));
   const int grid = max_chunks > 0 ? cols * hkv : 0;
   const int target = std::max(1, kUnitsPerWorkgroup * std::max(grid, 1));
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, cu_k, seg_indptr,
-                     (const Segment*)segs, batch, hkv, forced_len, min_len, target, max_chunks, max_k,
-                     hdr, chunk_base, recs);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // The split workgroups plan for themselves when the batch fits one request per thread, the
+  // chunk length is automatic and every column's units fit the LDS table: at most
+  // (kUnitsPerWorkgroup * cols + 2 * batch) / cols of them (decode_auto_chunk_bound).
+  const bool in_plan = grid > 0 && forced_len <= 0 && batch <= kInPlanBatch &&
+                       kUnitsPerWorkgroup + (2 * batch + cols - 1) / cols <= kUnitCap &&
+                       !decode_plan_kernel_forced();
+  hipError_t e = hipSuccess;
+  if (!in_plan) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, cu_k, seg_indptr,
+                       (const Segment*)segs, batch, hkv, forced_len, min_len, target, max_chunks, max_k,
+                       hdr, chunk_base, recs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (grid > 0) {
     const float scale_log2 = scale * 1.4426950408889634f;
-    auto split = kv == 2 ? decode_split_kernel<2> : (kv == 1 ? decode_split_kernel<1> : decode_split_kernel<0>);
+    const InPlanArgs ipa{cu_k, seg_indptr, chunk_base, batch, min_len, target, max_chunks, max_k};
+    auto split = in_plan
+        ? (kv == 2 ? decode_split_kernel<2, true> : (kv == 1 ? decode_split_kernel<1, true> : decode_split_kernel<0, true>))
+        : (kv == 2 ? decode_split_kernel<2, false> : (kv == 1 ? decode_split_kernel<1, false> : decode_split_kernel<0, false>));
     hipLaunchKernelGGL(split, dim3(grid), dim3(kDecThreads), 0, stream, (const bf16_t*)q, k_pool,
-                       v_pool, k_scale, v_scale, (const Segment*)segs, hdr, recs, hkv, scale,
+                       v_pool, k_scale, v_scale, (const Segment*)segs, hdr, recs, ipa, hkv, scale,
                        scale_log2, ws_o, ws_lse, (bf16_t*)out, lse);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

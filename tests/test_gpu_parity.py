@@ -201,6 +201,57 @@ def test_decode_large_batches(batch, kvd):
     _full_compare(w, f"decode-B{batch}", num_splits=4)
 
 
+PLAN_PATH_CASES = [
+    # (seed, k_lens, max_segs, kv_dtype): more than 8 segments per request (the in-workgroup
+    # plan reads a request's segments 8 at a time), empty segments, 1-key requests
+    (51, [5000, 1, 3000, 64, 12000, 0, 777], 20, "bf16"),
+    (52, [40000, 3, 9000, 513], 30, "fp8_e4m3"),
+    (53, [1, 2, 3, 20000, 4096, 4097], 12, "int8"),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("case", PLAN_PATH_CASES, ids=[f"seed{c[0]}" for c in PLAN_PATH_CASES])
+def test_decode_plan_in_workgroup_matches_plan_kernel(case, monkeypatch):
+    """With the automatic chunk length, batches of up to 256 requests are planned inside the
+    split workgroups; the separate plan launch (SEG_ATTN_DECODE_PLAN=kernel) makes the same
+    chunks, so outputs and LSE agree bit for bit, for both decode entry points. The oracle
+    checks the in-workgroup result."""
+    import attention_segmented_kv_amd as sa
+    seed, kl, ms, kvd = case
+    print(f"[case] decode plan paths seed={seed} k={kl} {kvd}", flush=True)
+    w = wl.make_random(seed, batch=len(kl), q_lens=[1] * len(kl), k_lens=kl, max_segs=ms,
+                       kv_dtype=kvd, kind="decode", zero_length_segments=True).to("cuda")
+    kw = dict(k_scale=w.k_scale, v_scale=w.v_scale) if kvd != "bf16" else {}
+    res = {}
+    for path in ("workgroup", "kernel"):
+        if path == "kernel":
+            monkeypatch.setenv("SEG_ATTN_DECODE_PLAN", "kernel")
+        else:
+            monkeypatch.delenv("SEG_ATTN_DECODE_PLAN", raising=False)
+        res[path] = [f(w.q, w.k_pool, w.v_pool, w.segs, w.seg_indptr, w.cu_seqlens_k, w.max_seqlen_k,
+                       return_lse=True, **kw)
+                     for f in (sa.decode, sa.decode_noalloc)]
+        torch.cuda.synchronize()
+    monkeypatch.delenv("SEG_ATTN_DECODE_PLAN", raising=False)
+    for (oa, la), (ob, lb) in zip(res["workgroup"], res["kernel"]):
+        assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+        assert torch.equal(la.view(torch.int32), lb.view(torch.int32))
+    _full_compare(w, f"plan-paths-{seed}")
+
+
+@needs_gpu
+@pytest.mark.parametrize("batch", [256, 257])
+def test_decode_automatic_plan_at_the_batch_limit(batch):
+    """256 requests are planned in the workgroups, 257 by the plan kernel: both against the
+    oracle, with the automatic chunk length."""
+    print(f"[case] automatic decode plan B={batch}", flush=True)
+    kl = [int(x) for x in np.random.default_rng(60 + batch).integers(1, 3000, size=batch)]
+    w = wl.make_random(60 + batch, batch=batch, q_lens=[1] * batch, k_lens=kl, max_segs=3,
+                       kind="decode").to("cuda")
+    _full_compare(w, f"decode-auto-B{batch}")
+
+
 # ---------------------------------------------------------------- invariants on the device
 
 @needs_gpu
