@@ -128,6 +128,11 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
  *              ceil(max_seqlen_k / n) keys rounded up to a multiple of 64, so at most n per
  *              request. A request cut into one chunk is written directly; otherwise each chunk's
  *              partial (O_s, LSE_s) goes to the workspace and a merge kernel combines them.
+ *              The chunks are listed on the device: by the split workgroups themselves when
+ *              num_splits = 0 and batch <= 256, otherwise by a one-workgroup plan kernel
+ *              launched first. Both list the same chunks, so the results are the same bit for
+ *              bit; the environment variable SEG_ATTN_DECODE_PLAN=kernel selects the plan
+ *              kernel for every call.
  * out          [batch, Hq, 128] bf16; lse [batch, Hq] fp32 or NULL. A request with K_b = 0
  *              gets out = 0 and lse = -inf.
  * workspace    device scratch of at least seg_attn_decode_workspace_bytes(...) bytes for the
