@@ -1109,6 +1109,9 @@ __global__ __launch_bounds__(kFThreads) void la_fused_kernel(
   lds_char_t* lds = (lds_char_t*)lds_raw;
   lds_f32_t* Gl = (lds_f32_t*)(lds + kFGOff);
   lds_f32_t* wsum = Gl + kFusedMaxLen;  // the 4 wave totals of the prefix sum
+  // Every pointer argument in scalar registers before the first table read, so that the
+  // kernel-argument loads share one round trip instead of following the tables one by one.
+  asm volatile("" ::"s"(q), "s"(k), "s"(v), "s"(g), "s"(cu), "s"(slots), "s"(pool), "s"(out));
   // workgroup order: the state workgroups (quarter-major), then output tiles heaviest first,
   // (request, head) fastest throughout, so that with 8 | H every workgroup of head h runs on XCD
   // h % 8 and shares its L2
@@ -1118,9 +1121,17 @@ __global__ __launch_bounds__(kFThreads) void la_fused_kernel(
   const bool state_role = id < n_state;
   const int bh = state_role ? id % bh_count : (id - n_state) % bh_count;
   const int b = bh / H, h = bh - b * H;
-  const int64_t slot = slots[b];
+  // The request's slot and token range in one vector load (lanes 0-2), then broadcast: one
+  // round trip, where scalar loads would wait for the slot before reading cu.
+  int tv = 0;
+  {
+    const int tl = threadIdx.x & 63;
+    if (tl < 3) tv = tl == 0 ? slots[b] : cu[b + tl - 1];
+  }
+  const int64_t slot = __builtin_amdgcn_readlane(tv, 0);
+  const int t_begin = __builtin_amdgcn_readlane(tv, 1), t_end = __builtin_amdgcn_readlane(tv, 2);
   if (slot < 0 || slot >= pool_slots) return;  // the whole workgroup leaves together
-  const int t_begin = cu[b], n = cu[b + 1] - t_begin;
+  const int n = t_end - t_begin;
   if (state_role) {
     fused_state(lds, Gl, wsum, k, v, g, t_begin, n, H, h, id / bh_count, max_len, slot, initial_state, pool);
   } else {
