@@ -3,9 +3,10 @@
 // Work units. Each request's keys are cut into chunks of `len` keys (the last one shorter); a
 // unit is one (chunk, kv head) pair, whose result is the blockwise partial attention of the
 // FlashAccel article ("data layout": attention computed per block of the KV, then reduced per
-// request). A one-workgroup plan kernel lists the chunks of all requests on the device, so no
-// launch slot is spent on requests shorter than the longest, and chooses `len` from the total
-// key count so that every compute unit gets about 6 units.
+// request). The chunks of all requests are listed on the device, so no launch slot is spent on
+// requests shorter than the longest, with `len` chosen from the total key count so that every
+// compute unit gets about 6 units: by each split workgroup itself for up to 256 requests with
+// the automatic length, else by a one-workgroup plan kernel launched first.
 //
 // Split pass. One persistent workgroup per compute unit walks its share of the units. Its 4
 // waves split each unit's tiles round robin (tile i to wave i % 4) and stream them through a
