@@ -106,6 +106,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base) {
 __device__ __forceinline__ void copy16_buf(__amdgpu_buffer_rsrc_t r, lds_void_t* lds_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
 }
+// copy16_buf into lds_base + kImm, from byte offset voff (>= kImm): the instruction's immediate
+// offset moves both the LDS and the memory address, so copies into one region at constant
+// distances share one LDS base (M0) and the wave writes M0 once for all of them.
+template <int kImm>
+__device__ __forceinline__ void copy16_buf_at(__amdgpu_buffer_rsrc_t r, lds_void_t* lds_base, uint32_t voff) {
+  static_assert(kImm >= 0 && kImm < 4096, "immediate offset range");
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff - kImm, 0, kImm, 0);
+}
 // The same with the non-temporal bit (data read once, in a stream), and 4 bytes per lane.
 __device__ __forceinline__ void copy16_buf_stream(__amdgpu_buffer_rsrc_t r, lds_void_t* lds_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 2);

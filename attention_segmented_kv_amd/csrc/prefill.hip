@@ -218,8 +218,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     lds_char_t* l = (lds_char_t*)dst + wave * 2048;
     if ((kb0 + kBlockN <= K) && (last - kcur.start < kcur.len)) {
       const auto r = block_rsrc(kbase + ((int64_t)kcur.off + (kb0 - kcur.start)) * tok_stride);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) copy16_buf(r, (lds_void_t*)(l + 1024 * i), koff[i]);
+      copy16_buf_at<0>(r, (lds_void_t*)l, koff[0]);
+      copy16_buf_at<1024>(r, (lds_void_t*)l, koff[1]);  // koff[1] >= 4 rows >= 1024 bytes
     } else {
       SegCursor c2;
       c2.segs = kcur.segs; c2.idx = kcur.idx; c2.end = kcur.end;
@@ -240,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     lds_char_t* l = (lds_char_t*)dst + vdst0;
     if ((kb0 + kBlockN <= K) && (last - vcur.start < vcur.len)) {
       const auto r = block_rsrc(vbase + ((int64_t)vcur.off + (kb0 - vcur.start)) * tok_stride);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) copy16_buf(r, (lds_void_t*)(l + 1024 * i), voff[i]);
+      copy16_buf_at<0>(r, (lds_void_t*)l, voff[0]);
+      copy16_buf_at<1024>(r, (lds_void_t*)l, voff[1]);  // voff[1] >= 16 rows >= 1024 bytes
     } else {
       SegCursor c2;
       c2.segs = vcur.segs; c2.idx = vcur.idx; c2.end = vcur.end;
