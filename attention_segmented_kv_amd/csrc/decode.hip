@@ -600,7 +600,9 @@ __device__ __forceinline__ int column_units(int n_chunks, int P, int p) {
   return full_rounds + (last_pos < n_chunks - full_rounds * P ? 1 : 0);
 }
 
-// All threads of the workgroup call this. scr: LDS for 6 x 257 + 40 ints that no copy writes
+constexpr int kInPlanScrInts = 6 * 257 + 32;
+
+// All threads of the workgroup call this. scr: LDS for kInPlanScrInts ints that no copy writes
 // until it returns; utab: kUnitCap records of 3 x i32x4, laid out as the plan kernel's records.
 // Returns the chunk count, or -1 when some K_b exceeds max_k, the chunks would not fit in the
 // workspace (max_chunks) or a column would hold more than kUnitCap units; workgroup 0 then
@@ -770,6 +772,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   int n_chunks;
   if constexpr (kInPlan) {
     // the per-request values go to stage 1, which no copy fills before this returns
+    static_assert(kInPlanScrInts * 4 <= (int)sizeof(st1), "plan scratch exceeds stage 1");
     n_chunks = plan_in_workgroup(ipa.cu_k, ipa.seg_indptr, segs, ipa.batch, hkv, ipa.min_len,
                                  ipa.target_units, ipa.max_chunks, ipa.max_k, P, p,
                                  reinterpret_cast<int*>(st1), utab, hdr, ipa.chunk_base);
