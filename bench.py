@@ -391,12 +391,18 @@ def cpu_baseline(w, c: int):
 
 
 def measure(w, steps, warmup, kind, graph=False, loop_1000=False, per_call=True):
+    """Time one workload. The per-call loop (each call between its own events) and, for the
+    small prefills, the 1000-call loop run first and the W + K step loop last: the GPU's clocks
+    ramp up over the first tens of milliseconds of work, and a K-step loop that started right
+    after a cold start (with the few warmup steps a short run gives it) would time that ramp
+    instead of the kernels."""
     step = make_step(w)
-    t = time_steps(step, steps, warmup, graph)
+    t = {}
     if per_call:
         t.update(per_call_times(step))
     if loop_1000 and per_call:
         t["back_to_back_1000_us"] = back_to_back(step, 1000)
+    t.update(time_steps(step, steps, warmup, graph))
     if kind == "prefill":
         work = prefill_flops(w)
         achieved = work / (t["launch_ms_mean"] * 1e-3) / 1e12
