@@ -524,57 +524,76 @@ def main():
         "work_per_step": work,
     }
 
+    def guarded(name, fn):
+        # A secondary workload that raises is recorded as failed (and logged) instead of taking
+        # the headline's JSON line down with it; the headline above has already been measured.
+        try:
+            return fn()
+        except Exception as e:  # noqa: BLE001 - reported in the line, not swallowed
+            log(f"[bench] {name}: FAILED: {type(e).__name__}: {e}")
+            torch.cuda.synchronize()
+            return {"workload": name, "error": f"{type(e).__name__}: {e}"}
+
     if not args.quick:
         extra = []
         for c in (1, 2, 3, 4, 5, 6):
             if c == head_c:
                 continue
-            log(f"[bench] config {c}: generating")
-            wc = wl.make_config(c, device=dev)
-            v, u, rf, tc, wk = measure(wc, max(20, args.steps // 2), args.warmup, wc.kind, args.graph,
-                                       loop_1000=c in (1, 2), per_call=not args.no_per_call)
-            log(f"[bench] {wc.name}: {v:.2f} {u}, launch mean {tc['launch_ms_mean']*1e3:.1f} us, "
-                f"per-call median {tc.get('per_call_us_median', float('nan')):.1f} us, frac {rf['frac']:.3f}")
-            entry = {"workload": wc.name, "value": round(v, 3), "unit": u,
-                     "launch_us_mean": round(tc["launch_ms_mean"] * 1e3, 2),
-                     "timing": {k: round(x, 6) for k, x in tc.items()},
-                     "roofline": rf, "work_per_step": wk}
-            if not args.no_cpu_baseline:
-                log(f"[bench] {wc.name}: cpu baseline (oracle)")
-                entry["cpu_baseline"] = cpu_baseline(wc, c)
-                log(f"[bench] {wc.name}: oracle {entry['cpu_baseline']['value']:.4g} "
-                    f"{entry['cpu_baseline']['unit']} ({entry['cpu_baseline']['sample']})")
-            extra.append(entry)
-            del wc
+
+            def one_config(c=c):
+                log(f"[bench] config {c}: generating")
+                wc = wl.make_config(c, device=dev)
+                v, u, rf, tc, wk = measure(wc, max(20, args.steps // 2), args.warmup, wc.kind, args.graph,
+                                           loop_1000=c in (1, 2), per_call=not args.no_per_call)
+                log(f"[bench] {wc.name}: {v:.2f} {u}, launch mean {tc['launch_ms_mean']*1e3:.1f} us, "
+                    f"per-call median {tc.get('per_call_us_median', float('nan')):.1f} us, frac {rf['frac']:.3f}")
+                entry = {"workload": wc.name, "value": round(v, 3), "unit": u,
+                         "launch_us_mean": round(tc["launch_ms_mean"] * 1e3, 2),
+                         "timing": {k: round(x, 6) for k, x in tc.items()},
+                         "roofline": rf, "work_per_step": wk}
+                if not args.no_cpu_baseline:
+                    log(f"[bench] {wc.name}: cpu baseline (oracle)")
+                    entry["cpu_baseline"] = cpu_baseline(wc, c)
+                    log(f"[bench] {wc.name}: oracle {entry['cpu_baseline']['value']:.4g} "
+                        f"{entry['cpu_baseline']['unit']} ({entry['cpu_baseline']['sample']})")
+                return entry
+
+            extra.append(guarded(wl.CONFIG_NAMES[c], one_config))
             torch.cuda.empty_cache()
         result["configs"] = extra
         app = []
         for name, c, fmt in APPEND_CASES:
-            log(f"[bench] {name}: generating")
-            r = measure_append(name, c, fmt, max(20, args.steps // 2), args.warmup, dev)
-            log(f"[bench] {name}: {r['value']:.1f} GB/s, launch mean {r['launch_us_mean']:.2f} us, "
-                f"frac {r['roofline']['frac']:.3f}")
-            app.append(r)
+            def one_append(name=name, c=c, fmt=fmt):
+                log(f"[bench] {name}: generating")
+                r = measure_append(name, c, fmt, max(20, args.steps // 2), args.warmup, dev)
+                log(f"[bench] {name}: {r['value']:.1f} GB/s, launch mean {r['launch_us_mean']:.2f} us, "
+                    f"frac {r['roofline']['frac']:.3f}")
+                return r
+            app.append(guarded(name, one_append))
             torch.cuda.empty_cache()
         result["append"] = app
         lin = []
         for name in LINEAR_CASES:
-            log(f"[bench] {name}: generating")
-            r = measure_linear(name, max(20, args.steps // 2), args.warmup, dev)
-            rf = r["roofline"]
-            log(f"[bench] {name}: {r['value']:.2f} us, {rf['achieved']:.1f} {rf['unit']}, frac {rf['frac']:.3f}")
-            lin.append(r)
+            def one_linear(name=name):
+                log(f"[bench] {name}: generating")
+                r = measure_linear(name, max(20, args.steps // 2), args.warmup, dev)
+                rf = r["roofline"]
+                log(f"[bench] {name}: {r['value']:.2f} us, {rf['achieved']:.1f} {rf['unit']}, frac {rf['frac']:.3f}")
+                return r
+            lin.append(guarded(name, one_linear))
             torch.cuda.empty_cache()
         result["linear"] = lin
         log("[bench] allocator (host)")
-        result["allocator"] = measure_allocator()
-        log(f"[bench] allocator_decode_loop_b128: {result['allocator']['us_per_step']} us per step, "
-            f"{result['allocator']['segments_per_request_mean']} segments per request")
+        result["allocator"] = guarded("allocator_decode_loop_b128", measure_allocator)
+        if "error" not in result["allocator"]:
+            log(f"[bench] allocator_decode_loop_b128: {result['allocator']['us_per_step']} us per step, "
+                f"{result['allocator']['segments_per_request_mean']} segments per request")
 
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, head_c)
-        log(f"[bench] {w.name}: oracle {result['cpu_baseline']['value']:.4g} {result['cpu_baseline']['unit']}")
+        result["cpu_baseline"] = guarded(w.name + " cpu baseline", lambda: cpu_baseline(w, head_c))
+        if "error" not in result["cpu_baseline"]:
+            log(f"[bench] {w.name}: oracle {result['cpu_baseline']['value']:.4g} {result['cpu_baseline']['unit']}")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
