@@ -14,9 +14,14 @@ pytestmark = pytest.mark.gpu
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
 
 
-def _step_fn(w, out, lse, ws):
+def _step_fn(w, out, lse, ws, noalloc=False):
     import attention_segmented_kv_amd as sa
-    if w.kind == "prefill":
+    if noalloc:
+        def step():
+            sa.decode_noalloc(w.q, w.k_pool, w.v_pool, w.segs, w.seg_indptr, w.cu_seqlens_k, w.max_seqlen_k,
+                              k_scale=w.k_scale, v_scale=w.v_scale, softmax_scale=w.softmax_scale, out=out,
+                              lse=lse)
+    elif w.kind == "prefill":
         def step():
             sa.prefill(w.q, w.k_pool, w.v_pool, w.segs, w.seg_indptr, w.cu_seqlens_q, w.cu_seqlens_k,
                        w.max_seqlen_q, w.max_seqlen_k, causal=w.causal, softmax_scale=w.softmax_scale,
@@ -29,13 +34,13 @@ def _step_fn(w, out, lse, ws):
     return step
 
 
-def _check_replays(w, name):
+def _check_replays(w, name, noalloc=False):
     import attention_segmented_kv_amd as sa
     print(f"[case] graph replay {name}", flush=True)
     dev = w.q.device
     ws = None
     if w.kind == "decode":
-        kvd = sa.KV_FP8_E4M3 if w.kv_dtype == "fp8_e4m3" else sa.KV_BF16
+        kvd = {"fp8_e4m3": sa.KV_FP8_E4M3, "int8": sa.KV_INT8}.get(w.kv_dtype, sa.KV_BF16)
         need = sa.decode_workspace_bytes(w.batch, w.max_seqlen_k, w.num_heads_q, w.num_heads_kv,
                                          w.head_dim, kvd, 0)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -46,7 +51,7 @@ def _check_replays(w, name):
 
     out_g = torch.full_like(w.q, float("nan"))
     lse_g = torch.full((w.q.shape[0], w.q.shape[1]), float("nan"), dtype=torch.float32, device=dev)
-    step = _step_fn(w, out_g, lse_g, ws)
+    step = _step_fn(w, out_g, lse_g, ws, noalloc)
     step()  # warm up outside the capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -62,8 +67,8 @@ def _check_replays(w, name):
         torch.cuda.synchronize()
         assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), f"{name}: replay {r} output differs"
         assert torch.equal(lse_g.view(torch.int32), lse_e.view(torch.int32)), f"{name}: replay {r} lse differs"
-        # eager work on the same stream and workspace between replays
-        _step_fn(w, scratch, None, ws)()
+        # eager work on the same stream and workspace (or scratch) between replays
+        _step_fn(w, scratch, None, ws, noalloc)()
         torch.cuda.synchronize()
 
 
@@ -90,3 +95,21 @@ def test_graph_replay_decode_fp8():
     w = wl.make_random(13, batch=4, q_lens=[1] * 4, k_lens=[20000, 3, 9000, 512], kind="decode",
                        kv_dtype="fp8_e4m3", device="cuda")
     _check_replays(w, "decode fp8")
+
+
+@needs_gpu
+def test_graph_replay_decode_int8():
+    w = wl.make_random(14, batch=6, q_lens=[1] * 6, k_lens=[7000, 1, 300, 12000, 64, 2049], kind="decode",
+                       kv_dtype="int8", device="cuda")
+    _check_replays(w, "decode int8")
+
+
+@needs_gpu
+@pytest.mark.parametrize("kvd", ["bf16", "fp8_e4m3"])
+def test_graph_replay_decode_noalloc(kvd):
+    """The allocation-free decode is the entry point for callers that capture graphs: every
+    replay, with eager calls sharing its scratch in between, equals the eager result (and the
+    workspace decode's, which the eager reference in _check_replays is)."""
+    w = wl.make_random(15, batch=5, q_lens=[1] * 5, k_lens=[9000, 2, 640, 4097, 30000], kind="decode",
+                       kv_dtype=kvd, device="cuda")
+    _check_replays(w, f"decode_noalloc {kvd}", noalloc=True)
