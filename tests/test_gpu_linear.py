@@ -233,3 +233,57 @@ def test_linear_prefill_tokens_above_max_seqlen_give_nan(path, path_env):
     st = w.state_pool.detach().cpu()[w.state_slots.long().cpu()].double().numpy()
     assert np.isnan(st[0]).all() and np.isnan(st[2]).all()
     assert np.abs(st[1] - st_ref[1]).max() <= STATE_REL * np.abs(st_ref[1]).max()
+
+
+@needs_gpu
+@pytest.mark.parametrize("case", ["fused", "fused-state", "chunked-state", "decode"])
+def test_linear_graph_replays_equal_eager(case, path_env):
+    """A captured linear-attention call replayed several times (its state slots restored
+    before each replay, other eager calls in between) gives the eager outputs and final states
+    bit for bit: the timed form of these calls in the benchmark is such a replay."""
+    sa = _sa()
+    path_env("chunked" if case.startswith("chunked") else "fused")
+    print(f"[case] linear graph replay {case}", flush=True)
+    if case == "decode":
+        w = wl.make_linear(41, [1] * 9, kind="decode", initial_state=True, num_heads=4).to("cuda")
+    else:
+        w = wl.make_linear(42, [300, 77, 1], kind="prefill", initial_state=case.endswith("state"),
+                           num_heads=4).to("cuda")
+    out = torch.empty_like(w.q)
+    max_len = int(w.lens.max())
+    ws = None
+    if w.kind == "prefill":
+        need = sa._load().seg_attn_linear_prefill_workspace_bytes(w.batch, max_len, w.num_heads, 128)
+        ws = torch.empty(max(int(need), 256), dtype=torch.uint8, device="cuda")
+
+    def call(o):
+        if w.kind == "decode":
+            sa.linear_decode(w.q, w.k, w.v, w.g, w.state_slots, w.state_pool, scale=w.scale, out=o)
+        else:
+            sa.linear_prefill(w.q, w.k, w.v, w.g, w.cu_seqlens, w.state_slots, w.state_pool,
+                              initial_state=w.initial_state, scale=w.scale, out=o, max_seqlen=max_len,
+                              workspace=ws)
+
+    pool0 = w.state_pool.clone()
+    call(out)
+    torch.cuda.synchronize()
+    out_e, pool_e = out.clone(), w.state_pool.clone()
+    w.state_pool.copy_(pool0)
+    out_g = torch.empty_like(w.q)
+    call(out_g)  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out_g)
+    scratch = torch.empty_like(w.q)
+    for r in range(3):
+        w.state_pool.copy_(pool0)
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), f"{case}: replay {r} output"
+        assert torch.equal(w.state_pool.view(torch.int32), pool_e.view(torch.int32)), f"{case}: replay {r} states"
+        w.state_pool.copy_(pool0)
+        call(scratch)  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
