@@ -225,3 +225,46 @@ def test_append_is_deterministic_and_idempotent():
     torch.cuda.synchronize()
     for a, t in zip(first, (w.k_pool, w.v_pool, w.k_scale, w.v_scale)):
         assert np.array_equal(a, _raw(t))
+
+
+@needs_gpu
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3", "int8"])
+def test_append_graph_replays_equal_eager(fmt):
+    """A captured append (a decode step's tokens and a prefill chunk's) replayed into a pool
+    restored to its NaN-poisoned state each time writes the same bytes as the eager call: the
+    benchmark times the appends as such replays."""
+    sa = _sa()
+    print(f"[case] append graph replay {fmt}", flush=True)
+    k_lens = [300, 1, 900, 64]
+    n_new = np.array([1, 1, 257, 0], dtype=np.int64)
+    w = wl.make_random(61, batch=len(k_lens), q_lens=[1] * len(k_lens), k_lens=k_lens, max_segs=4,
+                       kind="decode", kv_dtype=fmt, zero_length_segments=True, device="cuda")
+    k_new = _new_rows(62, int(n_new.sum())).cuda()
+    v_new = _new_rows(63, int(n_new.sum())).cuda()
+    _, _, _, cu_new = _tables_and_counts(w, n_new)
+    cn = torch.as_tensor(cu_new.astype(np.int32)).cuda()
+    tensors = [t for t in (w.k_pool, w.v_pool, w.k_scale, w.v_scale) if t is not None]
+    before = [t.clone() for t in tensors]
+
+    def call():
+        sa.kv_append(k_new, v_new, w.segs, w.seg_indptr, cn, w.cu_seqlens_k, w.k_pool, w.v_pool,
+                     k_scale=w.k_scale, v_scale=w.v_scale)
+
+    call()
+    torch.cuda.synchronize()
+    eager = [_raw(t) for t in tensors]
+    for t, b in zip(tensors, before):
+        t.copy_(b)
+    call()  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(3):
+        for t, b in zip(tensors, before):
+            t.copy_(b)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, t in zip(eager, tensors):
+            assert np.array_equal(e, _raw(t)), f"{fmt}: replay {r} differs"
