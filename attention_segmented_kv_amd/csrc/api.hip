@@ -19,8 +19,8 @@ constexpr bool kDebugBuild = false;
 namespace segattn {
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool, const void* segs,
                           const int32_t* seg_indptr, const int32_t* cu_q, const int32_t* cu_k,
-                          int batch, int max_seqlen_q, int hkv, float scale, int causal, void* out,
-                          float* lse, int cu_count, int force_tile, hipStream_t stream);
+                          int batch, int max_seqlen_q, int hkv, int64_t pool_size, float scale, int causal,
+                          void* out, float* lse, int cu_count, int force_tile, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool,
                          const float* k_scale, const float* v_scale, int kv, const void* segs,
                          const int32_t* seg_indptr, const int32_t* cu_k, int batch, int hkv,
@@ -284,7 +284,7 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
                                                     pool_tokens, causal, (hipStream_t)stream);
     if (ts != SEG_ATTN_OK) return ts;
     hipError_t e = segattn::launch_prefill(q, k_pool, v_pool, segs, seg_indptr, cu_seqlens_q,
-                                           cu_seqlens_k, batch, max_seqlen_q, num_heads_kv,
+                                           cu_seqlens_k, batch, max_seqlen_q, num_heads_kv, pool_tokens,
                                            softmax_scale, causal, out, lse, current_cu_count(),
                                            prefill_tile_override(), (hipStream_t)stream);
     return e == hipSuccess ? SEG_ATTN_OK : SEG_ATTN_ERR_HIP;

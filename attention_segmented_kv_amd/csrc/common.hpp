@@ -109,6 +109,21 @@ __device__ __forceinline__ void copy16_buf(__amdgpu_buffer_rsrc_t r, lds_void_t*
 // copy16_buf into lds_base + kImm, from byte offset voff (>= kImm): the instruction's immediate
 // offset moves both the LDS and the memory address, so copies into one region at constant
 // distances share one LDS base (M0) and the wave writes M0 once for all of them.
+// 16 bytes per lane at byte offset off from base into LDS (lane L's bytes at lds_base + 16 * L),
+// for rows looked up one by one. With kOff32 (every offset used is below 4 GiB - 16) the load
+// goes through a raw buffer based at base; otherwise through a flat 64-bit address. The two land
+// the same bytes, but a flat copy into LDS makes the compiler treat every later LDS read as
+// possibly out of order and wait for all of them (lgkmcnt(0)) wherever one is used, while with
+// buffer copies only the kernel's own flat copies remain and it waits just for the reads needed.
+template <bool kOff32>
+__device__ __forceinline__ void copy16_row(const void* base, int64_t off, lds_void_t* lds_base) {
+  if constexpr (kOff32) {
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, (uint32_t)off, 0, 0, 0);
+  } else {
+    __builtin_amdgcn_global_load_lds((const char*)base + off, lds_base, 16, 0, 0);
+  }
+}
 template <int kImm>
 __device__ __forceinline__ void copy16_buf_at(__amdgpu_buffer_rsrc_t r, lds_void_t* lds_base, uint32_t voff) {
   static_assert(kImm >= 0 && kImm < 4096, "immediate offset range");

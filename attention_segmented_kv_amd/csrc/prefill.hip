@@ -111,7 +111,7 @@ __device__ __forceinline__ void mark_uncovered_rows(bf16_t* out, float* lse, int
 // wave's Q rows stay in registers.
 constexpr int kWidePos = 32;
 
-template <bool kCausal>
+template <bool kCausal, bool kOff32>
 __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_pool,
     const bf16_t* __restrict__ v_pool, const Segment* __restrict__ segs,
@@ -228,8 +228,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
       for (int i = 0; i < 2; ++i) {
         const int r = krow0 + 4 * i;
         const int64_t slot = c2.slot(min(kb0 + r, last));
-        copy16_to_lds((const char*)(kbase + slot * tok_stride) + ((kch ^ (r & 15)) << 4),
-                      (lds_void_t*)(l + 1024 * i));
+        copy16_row<kOff32>(kbase, slot * tok_bytes + ((kch ^ (r & 15)) << 4), (lds_void_t*)(l + 1024 * i));
       }
     }
   };
@@ -249,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int64_t slot = c2.slot(min(kb0 + vrow0 + 16 * i, last));
-        copy16_to_lds((const char*)(vbase + slot * tok_stride) + vcol, (lds_void_t*)(l + 1024 * i));
+        copy16_row<kOff32>(vbase, slot * tok_bytes + vcol, (lds_void_t*)(l + 1024 * i));
       }
     }
   };
@@ -442,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
 // block j is consumed, and one barrier per block hands a slot from the readers to the copier.
 constexpr int kQuadThreads = 256;
 
-template <bool kCausal>
+template <bool kCausal, bool kOff32>
 __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_pool,
     const bf16_t* __restrict__ v_pool, const Segment* __restrict__ segs,
@@ -584,8 +583,7 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
       for (int k = 0; k < 4; ++k) {
         const int r = krow0 + 4 * k;
         const int64_t slot = c2.slot(min(kb0 + r, last));
-        copy16_to_lds((const char*)(kbase + slot * tok_stride) + ((((lane & 15) ^ (r & 15))) << 4),
-                      (lds_void_t*)(lk + 1024 * k));
+        copy16_row<kOff32>(kbase, slot * tok_bytes + (((lane & 15) ^ (r & 15)) << 4), (lds_void_t*)(lk + 1024 * k));
       }
       c2.segs = cur.segs;
       c2.idx = cur.idx;
@@ -596,7 +594,7 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t slot = c2.slot(min(kb0 + vrow0 + 16 * k, last));
-        copy16_to_lds((const char*)(vbase + slot * tok_stride) + vcol, (lds_void_t*)(lv + 1024 * k));
+        copy16_row<kOff32>(vbase, slot * tok_bytes + vcol, (lds_void_t*)(lv + 1024 * k));
       }
     }
     return pc;
@@ -643,18 +641,19 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // V^T operands of the first d tile, read while the softmax runs
-    auto read_vt = [&](int dt, bf16x8 (&dst)[4]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        bf16x4 lo = lds_read_tr16(vb + vlane + (dt * 4096 + u * 1024));
-        bf16x4 hi = lds_read_tr16(vb + vlane + (dt * 4096 + u * 1024 + 512));
-        dst[u][0] = lo[0]; dst[u][1] = lo[1]; dst[u][2] = lo[2]; dst[u][3] = lo[3];
-        dst[u][4] = hi[0]; dst[u][5] = hi[1]; dst[u][6] = hi[2]; dst[u][7] = hi[3];
-      }
+    // V^T operand i of the block (d tile i / 4, key step i % 4): two transposing reads. The
+    // PV MFMAs take them in order from a ring of 8, each read kLead MFMAs ahead of its use, so
+    // that at most 2 * kLead + 2 reads are in flight and the wait before MFMA i can leave the
+    // later ones pending (the LDS counter holds at most 15).
+    constexpr int kLead = 6;
+    auto read_vt = [&](int i) __attribute__((always_inline)) {
+      bf16x4 lo = lds_read_tr16(vb + vlane + ((i >> 2) * 4096 + (i & 3) * 1024));
+      bf16x4 hi = lds_read_tr16(vb + vlane + ((i >> 2) * 4096 + (i & 3) * 1024 + 512));
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    bf16x8 va[2][4];
-    read_vt(0, va[0]);
+    bf16x8 va[8];
+#pragma unroll
+    for (int i = 0; i < kLead; ++i) va[i] = read_vt(i);
 
     // ---- online softmax of the block (keys on the M side: a lane holds 32 scores of its row)
     const int kb0 = blk * kBlockN;
@@ -702,12 +701,11 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
 
     // ---- O^T[d][row] += V^T P^T
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      if (dt + 1 < 4) read_vt(dt + 1, va[(dt + 1) & 1]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) o[dt] = mfma32x32x16(va[dt & 1][u], pb[u], o[dt]);
-      if (dt + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    for (int i = 0; i < 16; ++i) {
+      o[i >> 2] = mfma32x32x16(va[i & 7], pb[i & 3], o[i >> 2]);
+      if (i + kLead < 16) va[(i + kLead) & 7] = read_vt(i + kLead);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kLead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -783,15 +781,20 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
 // more compute units busy on small batches. SEG_ATTN_PREFILL_TILE=128|256 forces one of them.
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool, const void* segs,
                           const int32_t* seg_indptr, const int32_t* cu_q, const int32_t* cu_k,
-                          int batch, int max_seqlen_q, int hkv, float scale, int causal, void* out,
-                          float* lse, int cu_count, int force_tile, hipStream_t stream) {
+                          int batch, int max_seqlen_q, int hkv, int64_t pool_size, float scale, int causal,
+                          void* out, float* lse, int cu_count, int force_tile, hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
+  // Rows looked up one by one are copied through a buffer when every byte offset from a kv head's
+  // first pool row fits in 32 bits (pools up to 16M token x kv-head rows), else through flat
+  // addresses.
+  const bool off32 = pool_size * hkv * kHeadDim * 2 <= 0xFFFFFFF0LL;
   const int64_t wide_tiles = (int64_t)((max_seqlen_q + kWidePos - 1) / kWidePos) * hkv * batch;
   const bool wide = force_tile == 256 || (force_tile != 128 && wide_tiles >= 2LL * cu_count);
   if (wide) {
     const int n_qtiles = (max_seqlen_q + kWidePos - 1) / kWidePos;
     if (wide_tiles == 0) return hipSuccess;
-    auto kern = causal ? prefill_wide_kernel<true> : prefill_wide_kernel<false>;
+    auto kern = causal ? (off32 ? prefill_wide_kernel<true, true> : prefill_wide_kernel<true, false>)
+                       : (off32 ? prefill_wide_kernel<false, true> : prefill_wide_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)wide_tiles), dim3(kThreads), 0, stream, (const bf16_t*)q,
                        (const bf16_t*)k_pool, (const bf16_t*)v_pool, (const Segment*)segs, seg_indptr,
                        cu_q, cu_k, batch, hkv, n_qtiles, scale, scale_log2, (bf16_t*)out, lse);
@@ -800,7 +803,8 @@ hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
   const int n_qtiles = (max_seqlen_q + kPosPerTile - 1) / kPosPerTile;
   const int64_t grid = (int64_t)n_qtiles * hkv * batch;
   if (grid == 0) return hipSuccess;
-  auto kern = causal ? prefill_quad_kernel<true> : prefill_quad_kernel<false>;
+  auto kern = causal ? (off32 ? prefill_quad_kernel<true, true> : prefill_quad_kernel<true, false>)
+                     : (off32 ? prefill_quad_kernel<false, true> : prefill_quad_kernel<false, false>);
   const int fold = (causal && grid <= 2LL * cu_count) ? (n_qtiles + 1) / 2 : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kQuadThreads), 0, stream, (const bf16_t*)q,
                      (const bf16_t*)k_pool, (const bf16_t*)v_pool, (const Segment*)segs, seg_indptr,
