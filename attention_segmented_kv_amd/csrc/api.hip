@@ -264,7 +264,7 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
   try {
     if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || pool_tokens < 0) return SEG_ATTN_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return SEG_ATTN_ERR_INVALID_ARG;
-    if (!std::isfinite(softmax_scale)) return SEG_ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return SEG_ATTN_ERR_INVALID_ARG;
     seg_attn_status_t hs = check_heads(num_heads_q, num_heads_kv, head_dim);
     if (hs != SEG_ATTN_OK) return hs;
     if (causal && max_seqlen_q > max_seqlen_k) return SEG_ATTN_ERR_INVALID_ARG;
@@ -366,7 +366,7 @@ seg_attn_status_t decode_impl(const void* q, const void* k_pool, const void* v_p
                               hipStream_t stream) {
   if (batch < 0 || max_seqlen_k < 0 || pool_tokens < 0 || num_splits < 0) return SEG_ATTN_ERR_INVALID_ARG;
   if (!valid_kv_dtype(kv_dtype)) return SEG_ATTN_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return SEG_ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return SEG_ATTN_ERR_INVALID_ARG;
   seg_attn_status_t hs = check_heads(num_heads_q, num_heads_kv, head_dim);
   if (hs != SEG_ATTN_OK) return hs;
   if (pool_tokens > INT32_MAX) return SEG_ATTN_ERR_UNSUPPORTED;

@@ -38,6 +38,9 @@ constexpr int kThreads = 512;    // 8 waves
 constexpr int kPosPerTile = 16;  // 4 waves x 32 rows / 8 heads
 constexpr int kBlkBytes = kBlockN * kHeadDim * 2;  // 16 KiB
 constexpr float kRescaleLog2 = 8.0f;
+// Running-max start: below any score, so that no infinity arithmetic is needed; a row that
+// never sees a key keeps it (and l = 0).
+constexpr float kNoMax = -3.0e38f;
 
 // LDS layouts (row = key within the block, 256 B = 16 chunks of 16 B per row):
 //   K: chunk c of row r is stored at chunk position c ^ (r % 16)
@@ -260,8 +263,10 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
   bf16x8 pb[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) pb[u] = bf16x8{};
-  float m_run = -INFINITY;
+  float m_run = kNoMax;
+  float neg = 0.f;  // -m_run * scale_log2 once m_run holds a score
   float l_run = 0.f;
+  const float grow_thr = kRescaleLog2 / scale_log2;  // move m_run when a block's max exceeds it by this
   const int G = lane >> 4;
   const int sl = lane & 15;
   // V^T operands (quarter-major V): lane reads rows 16 u + 4 h + sl / 4 (and + 8) at d offset
@@ -343,16 +348,17 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s1[e]);
     mx = max_xor32(mx);
-    const bool grow = (m_run == -INFINITY) ? (mx != -INFINITY) : ((mx - m_run) * scale_log2 > kRescaleLog2);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    // m_run starts at kNoMax, so the first block with a visible key always moves it (alpha is
+    // then 0) and no step tests for infinities; neg stays 0 while a row has seen no key
+    if (__builtin_amdgcn_ballot_w64(mx - m_run > grow_thr) != 0) {
       const float m_new = __builtin_fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * scale_log2);
+      const float alpha = fast_exp2((m_run - m_new) * scale_log2);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
       l_run *= alpha;
       m_run = m_new;
+      neg = m_run == kNoMax ? 0.f : -m_run * scale_log2;
     }
-    const float neg = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2;
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -611,8 +617,10 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY;
+  float m_run = kNoMax;
+  float neg = 0.f;  // -m_run * scale_log2 once m_run holds a score
   float l_run = 0.f;  // this lane's keys only; the row total is l + l of lane ^ 32
+  const float grow_thr = kRescaleLog2 / scale_log2;  // move m_run when a block's max exceeds it by this
 
   // One block: S^T = K Q^T, online softmax, O^T += V^T P^T. LDS operands are read ahead of the
   // MFMAs that use them (K two steps ahead, V one d tile ahead).
@@ -674,16 +682,17 @@ __global__ __launch_bounds__(kQuadThreads, 2) void prefill_quad_kernel(
     for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, s1[e]);
     mx = max_xor32(mx);
     // move the reference max only when the block's max clears it by 2^8 (exp2 units)
-    const bool grow = (m_run == -INFINITY) ? (mx != -INFINITY) : ((mx - m_run) * scale_log2 > kRescaleLog2);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    // m_run starts at kNoMax, so the first block with a visible key always moves it (alpha is
+    // then 0) and no step tests for infinities; neg stays 0 while a row has seen no key
+    if (__builtin_amdgcn_ballot_w64(mx - m_run > grow_thr) != 0) {
       const float m_new = __builtin_fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_new) * scale_log2);
+      const float alpha = fast_exp2((m_run - m_new) * scale_log2);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
       l_run *= alpha;
       m_run = m_new;
+      neg = m_run == kNoMax ? 0.f : -m_run * scale_log2;
     }
-    const float neg = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2;
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {

@@ -92,7 +92,8 @@ enum { SEG_ATTN_KV_BF16 = 0, SEG_ATTN_KV_FP8_E4M3 = 1, SEG_ATTN_KV_INT8 = 2 };
  *              written as NaN, so the broken bound shows in the output.
  * max_seqlen_k: HOST upper bound of every K_b; with causal, max_seqlen_q <= max_seqlen_k is
  *              required (INVALID_ARG otherwise). The kernels do not depend on it otherwise.
- * softmax_scale: multiplies Q K^T (1/sqrt(128) for the usual scaling).
+ * softmax_scale: multiplies Q K^T (1/sqrt(128) for the usual scaling); finite and > 0
+ *              (INVALID_ARG otherwise: masked keys are carried as -inf scores).
  * causal:      0 or 1. With causal and Lq_b > K_b the first Lq_b - K_b rows of request b see no
  *              key (seg_attn_validate_tables reports such tables).
  * out          [total_q, Hq, 128] bf16, written for every query row of every request; a row
@@ -119,6 +120,7 @@ seg_attn_status_t seg_attn_prefill(const void* q, const void* k_pool, const void
  * k_scale/v_scale [pool_tokens, Hkv] fp32 for FP8 and INT8 (required), ignored (may be NULL)
  *              for bf16. Codes are converted to bf16 exactly; k_scale multiplies the fp32
  *              scores and v_scale the fp32 probabilities before their bf16 rounding.
+ * softmax_scale: as for seg_attn_prefill (finite and > 0).
  * cu_seqlens_k [batch+1] int32; max_seqlen_k: HOST upper bound of every K_b; it sizes the
  *              workspace. If some K_b exceeds it, nothing is computed and every output and
  *              LSE of the call is written as NaN, so the broken bound shows in the output.

@@ -80,6 +80,7 @@ def _prefill_args(**over):
     (dict(q=None), 1), (dict(out=None), 1), (dict(segs=None), 1), (dict(batch=-1), 1),
     (dict(mq=-3), 1), (dict(d=64), 2), (dict(hq=32), 2), (dict(hq=60), 1), (dict(hkv=0), 1),
     (dict(causal=2), 1), (dict(mq=8, mk=4), 1), (dict(scale=float("nan")), 1), (dict(pool=-1), 1),
+    (dict(scale=0.0), 1), (dict(scale=-0.1), 1),
 ])
 def test_prefill_rejects_bad_arguments(over, status):
     lib = _lib()
@@ -115,6 +116,7 @@ def _decode_args(**over):
     (dict(q=None), 1), (dict(kvd=7), 1), (dict(kvd=1), 1), (dict(kvd=1, ks=1), 1), (dict(d=96), 2),
     (dict(ns=-1), 1), (dict(mk=-1), 1), (dict(ns=4), 3), (dict(ns=4, ws=1, wsb=16), 3),
     (dict(ns=0), 3), (dict(ns=1), 3), (dict(kvd=2), 1), (dict(kvd=2, vs=1), 1), (dict(kvd=3), 1),
+    (dict(scale=0.0), 1), (dict(scale=-0.1), 1), (dict(scale=float("inf")), 1),
 ])
 def test_decode_rejects_bad_arguments(over, status):
     lib = _lib()
