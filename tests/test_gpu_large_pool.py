@@ -33,12 +33,13 @@ def _layout():
 
 
 @needs_gpu
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("tile", ["128", "256"])
-def test_prefill_pool_beyond_4gib(tile, monkeypatch):
+def test_prefill_pool_beyond_4gib(tile, causal, monkeypatch):
     monkeypatch.setenv("SEG_ATTN_PREFILL_TILE", tile)
     lens, small, big = _layout()
     k_lens = [sum(x) for x in lens]
-    print(f"[case] prefill large pool tile={tile} k={k_lens} big offsets={big}", flush=True)
+    print(f"[case] prefill large pool tile={tile} causal={causal} k={k_lens} big offsets={big}", flush=True)
     g = torch.Generator().manual_seed(4242)
     total = sum(k_lens)
     q = torch.randn(total, HQ, D, generator=g).to(torch.bfloat16).cuda()
@@ -63,7 +64,7 @@ def test_prefill_pool_beyond_4gib(tile, monkeypatch):
     results = []
     for pool_tokens, offsets in ((4096, small), (BIG_POOL, big)):
         kp, vp, segs = place(pool_tokens, offsets)
-        out, lse = sa.prefill(q, kp, vp, segs, indptr, cu, cu, max(k_lens), max(k_lens), causal=True,
+        out, lse = sa.prefill(q, kp, vp, segs, indptr, cu, cu, max(k_lens), max(k_lens), causal=causal,
                               return_lse=True)
         torch.cuda.synchronize()
         results.append((out.cpu(), lse.cpu()))
@@ -79,10 +80,11 @@ def test_prefill_pool_beyond_4gib(tile, monkeypatch):
     k_bits, v_bits, segs_np = small_host
     cu_np = cu.cpu().numpy()
     o_ref, l_ref = oracle.attention(wl.bits(q), k_bits, v_bits, segs_np, indptr.cpu().numpy(), cu_np, cu_np,
-                                    num_heads_kv=HKV, softmax_scale=D ** -0.5, causal=True)
-    mx, rms = H.assert_close(o_small.float().numpy(), o_ref, f"large-pool-{tile}")
-    H.assert_lse_close(l_small.numpy(), l_ref, f"large-pool-{tile}")
-    print(f"[parity] large-pool-{tile}: layouts bit-identical, max_abs={mx:.3e} rms={rms:.3e}", flush=True)
+                                    num_heads_kv=HKV, softmax_scale=D ** -0.5, causal=causal)
+    name = f"large-pool-{tile}-{'causal' if causal else 'full'}"
+    mx, rms = H.assert_close(o_small.float().numpy(), o_ref, name)
+    H.assert_lse_close(l_small.numpy(), l_ref, name)
+    print(f"[parity] {name}: layouts bit-identical, max_abs={mx:.3e} rms={rms:.3e}", flush=True)
 
 
 DEC_LENS = [[500, 300], [1], [77, 900, 3]]
