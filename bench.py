@@ -440,8 +440,8 @@ def main():
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the segment-attention path is built and timed on a single "
-              "MI355X; runs on more than one GPU are not part of this build.", file=sys.stderr)
+        print("bench.py measures one GPU: the segment-attention library runs on a single MI355X "
+              "and has no multi-GPU mode (--gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
