@@ -350,7 +350,7 @@ def blas_threads() -> int:
 # The oracle's sample per workload: (requests to evaluate, None = all; passes; how it is named).
 # Prefill samples take whole requests (every head and query row); decode samples whole requests
 # (every head). Sizes keep each sample at a few seconds to a few tens of seconds of host work.
-CPU_SAMPLES = {1: (None, 3), 2: (None, 3), 3: ([0], 1), 4: (None, 1), 5: ([0, 1], 1), 6: ([0, 1], 1)}
+CPU_SAMPLES = {1: (None, 3), 2: (None, 25), 3: ([0], 1), 4: (None, 1), 5: ([0, 1], 1), 6: ([0, 1], 1)}
 
 
 def cpu_baseline(w, c: int):
