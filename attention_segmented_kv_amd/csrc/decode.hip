@@ -98,6 +98,16 @@ __device__ __forceinline__ void int8x4_to_f16(uint32_t w, f16x2& a, f16x2& b) {
   b = __builtin_bit_cast(f16x2, hi) + off;
 }
 
+// The same 4 codes as the 4 halves c + 1152 (the conversion above without its subtraction), for
+// K: the scores built from them are corrected by 1152 * sum_d q_d of their head afterwards, once
+// per score instead of once per code.
+__device__ __forceinline__ void int8x4_to_f16_biased(uint32_t w, f16x2& a, f16x2& b) {
+  const uint32_t u = w ^ 0x80808080u;
+  a = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
+  b = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
+}
+constexpr float kInt8Bias = 1152.0f;
+
 // 8 one-byte codes (bytes 0..3 of lo, then of hi) as 8 exact MFMA operand values.
 template <int kKv>
 __device__ __forceinline__ OpT<kKv> codes8_to_op(uint32_t lo, uint32_t hi) {
@@ -107,6 +117,19 @@ __device__ __forceinline__ OpT<kKv> codes8_to_op(uint32_t lo, uint32_t hi) {
     f16x2 r[4];
     int8x4_to_f16(lo, r[0], r[1]);
     int8x4_to_f16(hi, r[2], r[3]);
+    return __builtin_bit_cast(f16x8, r);
+  }
+}
+
+// 8 one-byte K codes as MFMA operands: exact for FP8, plus kInt8Bias for INT8.
+template <int kKv>
+__device__ __forceinline__ OpT<kKv> kcodes8_to_op(uint32_t lo, uint32_t hi) {
+  if constexpr (kKv == 1) {
+    return fp8x8_to_bf16x8(lo, hi);
+  } else {
+    f16x2 r[4];
+    int8x4_to_f16_biased(lo, r[0], r[1]);
+    int8x4_to_f16_biased(hi, r[2], r[3]);
     return __builtin_bit_cast(f16x8, r);
   }
 }
@@ -988,6 +1011,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
   // ---- compute side
   OpT<kKv> qf[4];  // B operand of S^T: lane holds d = 32*step + 8*grp + (0..7) of head `col`
+  float kbias = 0.f;  // INT8: kInt8Bias * sum_d q_d of head `col` (the f16 q the MFMAs see)
   f32x4 o[8];
   float m_run, l_run;
   auto reset = [&]() __attribute__((always_inline)) {
@@ -1018,6 +1042,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     qf[1] = q_to_op<kKv>(real ? __builtin_bit_cast(bf16x8, v1) : bf16x8{});
     qf[2] = q_to_op<kKv>(real ? __builtin_bit_cast(bf16x8, v2) : bf16x8{});
     qf[3] = q_to_op<kKv>(real ? __builtin_bit_cast(bf16x8, v3) : bf16x8{});
+    if constexpr (kKv == 2) {
+      float qs = 0.f;
+#pragma unroll
+      for (int stp = 0; stp < 4; ++stp)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qs += (float)qf[stp][i];
+      kbias = kInt8Bias * sum_xor32(sum_xor16(qs));
+    }
   };
 
   // Combine the 4 waves' states for unit r and write the output or the partial.
@@ -1112,7 +1144,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
           const int c = byte >> 4;
           const __attribute__((address_space(3))) uint32_t* p =
               (const __attribute__((address_space(3))) uint32_t*)(kb + r * 128 + ((c ^ (r & 7)) << 4) + (byte & 15));
-          a = codes8_to_op<kKv>(p[0], p[1]);
+          a = kcodes8_to_op<kKv>(p[0], p[1]);
         }
         s[mt] = mfma_op(a, qf[stp], s[mt]);
       }
@@ -1123,6 +1155,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         const __attribute__((address_space(3))) f32x4* sp =
             (const __attribute__((address_space(3))) f32x4*)(vb + C::kKBytes + (16 * mt + 4 * grp) * 4);
         f32x4 sc = *sp;
+        if constexpr (kKv == 2) s[mt] -= f32x4{kbias, kbias, kbias, kbias};  // biased K codes
         s[mt] *= sc;
       }
     }
